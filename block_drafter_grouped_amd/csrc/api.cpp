@@ -1,0 +1,149 @@
+// C ABI of libdflash2: argument validation on the host, then kernel launches
+// on the caller's stream.  No allocation, no synchronisation, no state.
+#include <stdint.h>
+
+#include "../../include/dflash2.h"
+#include "kernels.h"
+
+namespace {
+
+using dfs::Dims;
+
+constexpr int kMaxRows = 65536;
+constexpr int kMaxHidden = 65536;
+constexpr int kMaxHiddenBf16Head = 8192;  // hidden rows stay resident in LDS
+constexpr int kMaxTapsF32 = 4096;         // fp32 conv keeps z and w in LDS (32 KB)
+
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
+int check_cfg(const dfs_config* c) {
+    if (!c) return DFS_ERR_NULL;
+    if (c->dtype != DFS_F32 && c->dtype != DFS_BF16) return DFS_ERR_UNSUPPORTED;
+    if (c->batch < 1 || c->block_size < 2 || c->block_size > 64) return DFS_ERR_SHAPE;
+    if ((int64_t)c->batch * c->block_size > kMaxRows) return DFS_ERR_SHAPE;
+    if (c->hidden < 32 || c->hidden % 32 != 0 || c->hidden > kMaxHidden) return DFS_ERR_SHAPE;
+    if (c->conv_group_size < 1 || c->hidden % c->conv_group_size != 0) return DFS_ERR_SHAPE;
+    if (c->conv_kernel_size < 1) return DFS_ERR_SHAPE;
+    if (c->conv_kernel_size != 1 && c->conv_kernel_size != 2 && c->conv_kernel_size != 4) return DFS_ERR_UNSUPPORTED;
+    if (c->top_k < 1) return DFS_ERR_SHAPE;
+    if (c->top_k > 64) return DFS_ERR_UNSUPPORTED;
+    if (c->vocab < c->top_k || c->vocab > INT32_MAX - 64) return DFS_ERR_SHAPE;
+    if (c->rank < 8 || c->rank % 8 != 0 || c->rank > 4096) return DFS_ERR_SHAPE;
+    if (c->dtype == DFS_BF16 && c->hidden > kMaxHiddenBf16Head) return DFS_ERR_UNSUPPORTED;
+    if (c->dtype == DFS_F32 && (int64_t)(c->hidden / c->conv_group_size) * c->conv_kernel_size > kMaxTapsF32)
+        return DFS_ERR_UNSUPPORTED;
+    return DFS_OK;
+}
+
+Dims dims_of(const dfs_config* c) {
+    return Dims{c->batch, c->block_size, c->hidden, c->vocab, c->top_k, c->rank, c->conv_group_size,
+                c->conv_kernel_size, c->dtype == DFS_BF16};
+}
+
+int check_ws(const dfs_config* c, const void* ws, size_t ws_bytes) {
+    const size_t need = dfs::ws_layout(dims_of(c)).total;
+    if (ws_bytes < need) return DFS_ERR_WORKSPACE;
+    if (need > 0 && !ws) return DFS_ERR_NULL;
+    if (misaligned(ws, 256)) return DFS_ERR_MISALIGNED;
+    return DFS_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DFS_OK : DFS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dfs_status_string(int status) {
+    switch (status) {
+        case DFS_OK: return "ok";
+        case DFS_ERR_NULL: return "a required pointer is NULL";
+        case DFS_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case DFS_ERR_UNSUPPORTED: return "value not supported by this build";
+        case DFS_ERR_MISALIGNED: return "tensor not 16-byte aligned (workspace: 256-byte)";
+        case DFS_ERR_WORKSPACE: return "workspace smaller than dfs_workspace_size()";
+        case DFS_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int dfs_validate_config(const dfs_config* cfg) { return check_cfg(cfg); }
+
+size_t dfs_workspace_size(const dfs_config* cfg) {
+    if (check_cfg(cfg) != DFS_OK) return 0;
+    return dfs::ws_layout(dims_of(cfg)).total;
+}
+
+int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm, void* y, float* y_f32, void* stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!h || !wg_cm || !y) return DFS_ERR_NULL;
+    if (misaligned(h, 16) || misaligned(wg_cm, 16) || misaligned(y, 16) || misaligned(y_f32, 16))
+        return DFS_ERR_MISALIGNED;
+    return hip_status(dfs::launch_conv(dims_of(cfg), h, wg_cm, y, y_f32, (hipStream_t)stream));
+}
+
+int dfs_head_topk(const dfs_config* cfg, const void* y, const void* W, int32_t* cand_ids, float* cand_logp,
+                  float* lse, float* logits_f32, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!y || !W || !cand_ids || !cand_logp || !lse) return DFS_ERR_NULL;
+    if (misaligned(y, 16) || misaligned(W, 16) || misaligned(cand_ids, 16) || misaligned(cand_logp, 16) ||
+        misaligned(lse, 16) || misaligned(logits_f32, 16))
+        return DFS_ERR_MISALIGNED;
+    if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+    return hip_status(dfs::launch_head_topk(dims_of(cfg), y, W, cand_ids, cand_logp, lse, logits_f32, (char*)ws,
+                                            (hipStream_t)stream));
+}
+
+int dfs_topk_logits(const dfs_config* cfg, const float* logits, int32_t* cand_ids, float* cand_logp, float* lse,
+                    void* ws, size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!logits || !cand_ids || !cand_logp || !lse) return DFS_ERR_NULL;
+    if (misaligned(logits, 16) || misaligned(cand_ids, 16) || misaligned(cand_logp, 16) || misaligned(lse, 16))
+        return DFS_ERR_MISALIGNED;
+    if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+    return hip_status(
+        dfs::launch_topk_logits(dims_of(cfg), logits, cand_ids, cand_logp, lse, (char*)ws, (hipStream_t)stream));
+}
+
+int dfs_select(const dfs_config* cfg, const int32_t* anchor, const int32_t* cand_ids, const float* cand_logp,
+               const void* P, const void* Q, int32_t* path, float* path_score, int32_t* path_idx, void* ws,
+               size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!anchor || !cand_ids || !cand_logp || !P || !Q || !path || !path_score) return DFS_ERR_NULL;
+    if (misaligned(anchor, 16) || misaligned(cand_ids, 16) || misaligned(cand_logp, 16) || misaligned(P, 16) ||
+        misaligned(Q, 16) || misaligned(path, 16) || misaligned(path_score, 16) || misaligned(path_idx, 16))
+        return DFS_ERR_MISALIGNED;
+    if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+    return hip_status(dfs::launch_select(dims_of(cfg), anchor, cand_ids, cand_logp, P, Q, path, path_score, path_idx,
+                                         (char*)ws, (hipStream_t)stream));
+}
+
+int dfs_draft_block(const dfs_config* cfg, const void* h, const int32_t* anchor, const void* wg_cm, const void* W,
+                    const void* P, const void* Q, int32_t* path, float* path_score, int32_t* cand_ids,
+                    float* cand_logp, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!h || !anchor || !wg_cm || !W || !P || !Q || !path || !path_score) return DFS_ERR_NULL;
+    if (misaligned(h, 16) || misaligned(anchor, 16) || misaligned(wg_cm, 16) || misaligned(W, 16) ||
+        misaligned(P, 16) || misaligned(Q, 16) || misaligned(path, 16) || misaligned(path_score, 16) ||
+        misaligned(cand_ids, 16) || misaligned(cand_logp, 16))
+        return DFS_ERR_MISALIGNED;
+    if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+    const Dims d = dims_of(cfg);
+    const dfs::WsLayout L = dfs::ws_layout(d);
+    char* w = (char*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    void* y = w + L.y;
+    int32_t* cids = cand_ids ? cand_ids : (int32_t*)(w + L.cids);
+    float* clogp = cand_logp ? cand_logp : (float*)(w + L.clogp);
+    float* lse = (float*)(w + L.lse);
+    if ((st = hip_status(dfs::launch_conv(d, h, wg_cm, y, nullptr, s)))) return st;
+    if ((st = hip_status(dfs::launch_head_topk(d, y, W, cids, clogp, lse, nullptr, w, s)))) return st;
+    return hip_status(dfs::launch_select(d, anchor, cids, clogp, P, Q, path, path_score, nullptr, w, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Launchers of the gfx950 kernels (host side).  Each enqueues on `stream`
+// and returns hipGetLastError() of its launches.  Arguments are validated by
+// the C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dfs {
+
+struct Dims {
+    int batch, B, D, V, K, r, gs, ks;
+    bool bf16;
+    int rows() const { return batch * B; }
+    int groups() const { return D / gs; }
+    int taps() const { return groups() * ks; }  // columns of the generator
+};
+
+// Number of vocabulary chunks whose per-chunk top-K / (max, sum) partials the
+// head writes.  A function of the shape only, so workspace sizes need no
+// device query.
+int head_chunks(const Dims& d);
+
+// Workspace carve-up (byte offsets from the 256-B aligned base).
+struct WsLayout {
+    size_t y, keys, ms, logits, T, cids, clogp, lse, total;
+};
+WsLayout ws_layout(const Dims& d);
+
+hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32,
+                       hipStream_t s);
+
+// Head + top-K.  Uses ws.keys / ws.ms (and ws.logits for fp32 if logits_f32
+// is NULL).
+hipError_t launch_head_topk(const Dims& d, const void* y, const void* W, int32_t* cand_ids,
+                            float* cand_logp, float* lse, float* logits_f32, char* ws,
+                            hipStream_t s);
+
+hipError_t launch_topk_logits(const Dims& d, const float* logits, int32_t* cand_ids, float* cand_logp,
+                              float* lse, char* ws, hipStream_t s);
+
+hipError_t launch_select(const Dims& d, const int32_t* anchor, const int32_t* cand_ids,
+                         const float* cand_logp, const void* P, const void* Q, int32_t* path,
+                         float* path_score, int32_t* path_idx, char* ws, hipStream_t s);
+
+}  // namespace dfs

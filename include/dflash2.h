@@ -1,0 +1,196 @@
+/*
+ * dflash2.h -- C ABI of libdflash2, the MI355X (gfx950) draft-block hot path
+ * of DFlash2 speculative decoding.
+ *
+ * One call turns the draft model's final hidden states for a block of B
+ * positions (slot 0 = the last verified token, the "anchor"; slots 1..B-1 =
+ * draft slots) into one proposed token path:
+ *
+ *   1. grouped dynamic depthwise causal conv inside the block
+ *      (vLLM release-note article on DFlash2, section "two additions");
+ *   2. vocabulary head (the target's lm_head) with log-softmax, over all rows;
+ *   3. per-slot top-K candidates over the full vocabulary
+ *      (same section: "keep the target head's top-K per slot");
+ *   4. low-rank adjacent-transition scores <P[a], Q[b]> between the
+ *      candidates of neighbouring slots (Inco AI post "DFlash 2: keep the
+ *      draft parallel", section "lightweight path selector", with the
+ *      context gate taken as 1);
+ *   5. the best path through the candidates, walked from the anchor
+ *      (release-note article, "two additions"), as max-sum Viterbi.
+ *
+ * Constants of the published checkpoint (RTX 4090 report, section 4,
+ * dflash_config): block_size 8, conv_group_size 16, conv_kernel_size 2,
+ * selector_rank 256, selector_top_k 16.  block_size = 1 + draft tokens.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - `cfg` is a HOST pointer.  Every tensor pointer is a DEVICE pointer to
+ *    row-major, contiguous memory, 16-byte aligned; the workspace is 256-byte
+ *    aligned.  Rows of block b are b*B .. b*B+B-1 (rows = batch * B).
+ *  - Floating tensors (h, wg_cm, y, W, P, Q) have the dtype cfg->dtype:
+ *    DFS_BF16 (the hot path: bf16 inputs, fp32 accumulation) or DFS_F32 (a
+ *    plain correctness path).  Candidate scores, lse and logits are fp32;
+ *    ids are int32.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    validates its arguments on the host and enqueues kernels on `stream`:
+ *    it never allocates, frees or synchronises, and returns before the work
+ *    is done.  The caller synchronises before reading outputs.
+ *  - Ownership: the caller owns every buffer, including the workspace
+ *    (>= dfs_workspace_size(cfg) bytes; contents undefined between calls;
+ *    one call at a time per workspace).  The library keeps no state.
+ *  - Errors: the return value is a dfs_status.  All argument checks happen on
+ *    the host BEFORE any HIP call, so a rejected call touches no device
+ *    state.  DFS_ERR_HIP reports a failed kernel launch; faults inside a
+ *    kernel surface at the caller's synchronisation.
+ *  - Results are bit-identical from run to run (no atomics in any sum).
+ *  - Ties: candidates with equal logits are ordered by lower vocabulary id
+ *    (-0.0 and +0.0 are equal); the walk takes the lowest predecessor index
+ *    and the lowest final index among equal scores.  NaN inputs are not
+ *    supported.
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DFS_OK = 0,
+    DFS_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    DFS_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
+    DFS_ERR_UNSUPPORTED = 3, /* a valid value this build does not implement    */
+    DFS_ERR_MISALIGNED = 4,  /* a tensor is not 16-B (workspace: 256-B) aligned */
+    DFS_ERR_WORKSPACE = 5,   /* ws_bytes < dfs_workspace_size(cfg)             */
+    DFS_ERR_HIP = 6          /* a kernel launch failed                         */
+} dfs_status;
+
+typedef enum { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype;
+
+/* Field names follow the checkpoint's dflash_config where one exists. */
+typedef struct {
+    int32_t batch;            /* independent blocks, >= 1                         */
+    int32_t block_size;       /* B = 1 + draft slots, 2..64                       */
+    int32_t hidden;           /* D, a multiple of 32 and of conv_group_size       */
+    int32_t vocab;            /* V, top_k <= V < 2^31 - 1                          */
+    int32_t top_k;            /* K = selector_top_k, 1..64                         */
+    int32_t rank;             /* r = selector_rank, a multiple of 8, 8..4096       */
+    int32_t conv_group_size;  /* channels sharing one generated kernel (16)        */
+    int32_t conv_kernel_size; /* causal taps: 1, 2 or 4 (1 = identity conv)        */
+    int32_t dtype;            /* dfs_dtype                                         */
+} dfs_config;
+
+/* Bytes of workspace any entry point needs for `cfg` (0 if cfg is invalid). */
+size_t dfs_workspace_size(const dfs_config* cfg);
+
+/* Static description of a status code (never NULL). */
+const char* dfs_status_string(int status);
+
+/* Checks `cfg` alone (no pointers).  DFS_OK or the first violated rule. */
+int dfs_validate_config(const dfs_config* cfg);
+
+/*
+ * Step 1: grouped dynamic depthwise causal conv (release-note article,
+ * "two additions": a per-position kernel generated from the hidden state,
+ * shared by each group of conv_group_size channels, over the current and the
+ * earlier positions of the same block).
+ *
+ *   z[row, g*ks + j] = sum_c h[row, c] * wg_cm[g*ks + j, c]
+ *   w[row, g, :]     = softmax over the ks taps of z[row, g*ks : g*ks+ks]
+ *   y[b, t, c]       = sum_{j < ks, t-j >= 0} w[b*B+t, c / conv_group_size, j] * h[b, t-j, c]
+ *
+ *  h      [rows, D]     dtype, hidden states (row-major, block-major rows)
+ *  wg_cm  [G*ks, D]     dtype, generator weights, channel-major: row g*ks+j
+ *                       holds the weights of tap j of group g over all D
+ *                       channels (the transpose of the [D, G*ks] matrix)
+ *  y      [rows, D]     dtype, output; bf16 is the round-to-nearest-even of
+ *                       the fp32 result
+ *  y_f32  [rows, D]     fp32, optional (NULL): the fp32 result before
+ *                       rounding, for parity checks
+ * Positions before the start of a block count as zero; the tap softmax is
+ * not renormalised there.  Needs no workspace.
+ */
+int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm,
+             void* y, float* y_f32, void* stream);
+
+/*
+ * Steps 2-3: vocabulary head, log-softmax and per-slot top-K for every row.
+ *
+ *   logit[row, v] = sum_c y[row, c] * W[v, c]           (fp32 accumulation)
+ *   lse[row]      = log sum_v exp(logit[row, v])
+ *   cand_ids[row, :K]  the K largest logits, by (logit desc, id asc)
+ *   cand_logp[row, k]  = logit[row, cand_ids[row, k]] - lse[row]
+ *
+ *  y          [rows, D]  dtype (the conv output)
+ *  W          [V, D]     dtype, the shared target lm_head
+ *  cand_ids   [rows, K]  int32 out
+ *  cand_logp  [rows, K]  fp32 out
+ *  lse        [rows]     fp32 out
+ *  logits_f32 [rows, V]  fp32, optional (NULL): also writes every logit (the
+ *                        exact values the top-K was taken from), for parity
+ *  ws, ws_bytes          workspace (see conventions)
+ * The logits are never materialised otherwise: each workgroup keeps its own
+ * top-K and (max, sum of exp) partials, merged by a second kernel.
+ */
+int dfs_head_topk(const dfs_config* cfg, const void* y, const void* W,
+                  int32_t* cand_ids, float* cand_logp, float* lse,
+                  float* logits_f32, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 3 alone, on caller-supplied fp32 logits [rows, V] (any finite values
+ * or -inf; a row of all -inf yields lse = -inf and NaN scores).  Same outputs
+ * and ordering as dfs_head_topk.  cfg->dtype is ignored.
+ */
+int dfs_topk_logits(const dfs_config* cfg, const float* logits,
+                    int32_t* cand_ids, float* cand_logp, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Steps 4-5: transition scores and the best path (Inco AI post, section
+ * "lightweight path selector": every adjacent candidate pair is scored at
+ * once; the only sequential work is the walk over the precomputed scores,
+ * starting from the last verified token).
+ *
+ * For block b with candidates c_t = cand_ids[b*B + t, :] (t >= 1) and
+ * c_0 = {anchor[b]}:
+ *   T_t[j, k] = sum_i P[c_{t-1, j}, i] * Q[c_{t, k}, i]      (fp32 accumulation)
+ *   delta_1[k] = cand_logp[b*B+1, k] + T_1[0, k]
+ *   delta_t[k] = max_j (delta_{t-1}[j] + T_t[j, k]) + cand_logp[b*B+t, k]
+ * The path takes argmax_k delta_{B-1}[k] and backtracks; ties go to the
+ * lowest index at every step.
+ *
+ *  anchor     [batch]     int32, the verified token of each block
+ *  cand_ids   [rows, K]   int32, cand_logp [rows, K] fp32 (rows of slot 0 are
+ *                         not read)
+ *  P, Q       [V, r]      dtype: per-token selector embeddings; P is indexed
+ *                         by the predecessor, Q by the successor
+ *  path       [batch, B]  int32 out: path[b, 0] = anchor[b], then one
+ *                         candidate id per draft slot
+ *  path_score [batch]     fp32 out: delta_{B-1} of the chosen path
+ *  path_idx   [batch, B]  int32, optional: path_idx[b, 0] = -1, then the
+ *                         chosen candidate index per draft slot
+ * A block whose anchor lies outside [0, V) gets path = -1 in every slot,
+ * path_idx = -1 and path_score = NaN; the other blocks are unaffected.
+ */
+int dfs_select(const dfs_config* cfg, const int32_t* anchor,
+               const int32_t* cand_ids, const float* cand_logp,
+               const void* P, const void* Q, int32_t* path, float* path_score,
+               int32_t* path_idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole block: dfs_conv -> dfs_head_topk -> dfs_select on one stream.
+ * cand_ids / cand_logp are optional outputs (NULL: kept in the workspace).
+ * Arguments as above.
+ */
+int dfs_draft_block(const dfs_config* cfg, const void* h, const int32_t* anchor,
+                    const void* wg_cm, const void* W, const void* P, const void* Q,
+                    int32_t* path, float* path_score, int32_t* cand_ids,
+                    float* cand_logp, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH2_H */

@@ -1,0 +1,182 @@
+"""The C ABI on the host: exports, config rules, and every status a call can
+return before it touches the GPU.  Pointers here are fake addresses; every
+case is rejected by host-side validation, so no kernel is ever launched."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash2.h")
+
+dfs = pytest.importorskip("block_drafter_grouped_amd")
+import workloads as wl  # noqa: E402
+
+OK, NULL, SHAPE, UNSUP, MISAL, WS, HIP = range(7)
+A = 0x7F0000000000  # 256-B aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dfs_\w+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert set(names) == set(dfs.dflash2.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", dfs.dflash2.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dfs_\w+)$", out, re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(dfs.lib(), n)
+
+
+def test_status_strings():
+    for st in range(7):
+        s = dfs.lib().dfs_status_string(st)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert dfs.lib().dfs_status_string(99) == b"unknown status"
+
+
+def cfg_of(cfg_id=2, **kw):
+    c = dfs.Config.of(wl.shape_of(cfg_id))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("cfg_id", range(5))
+def test_workload_configs_are_valid(cfg_id):
+    c = cfg_of(cfg_id)
+    assert dfs.validate_config(c) == OK
+    assert dfs.workspace_size(c) > 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, SHAPE), ("block_size", 1, SHAPE), ("block_size", 65, SHAPE),
+    ("hidden", 48, SHAPE), ("hidden", 0, SHAPE), ("hidden", 16384, UNSUP),
+    ("conv_group_size", 0, SHAPE), ("conv_group_size", 48, SHAPE),
+    ("conv_kernel_size", 0, SHAPE), ("conv_kernel_size", 3, UNSUP), ("conv_kernel_size", 8, UNSUP),
+    ("top_k", 0, SHAPE), ("top_k", 65, UNSUP), ("vocab", 15, SHAPE),
+    ("rank", 0, SHAPE), ("rank", 12, SHAPE), ("rank", 8192, SHAPE), ("dtype", 7, UNSUP),
+])
+def test_config_rules(field, value, status):
+    c = cfg_of(2, **{field: value})
+    assert dfs.validate_config(c) == status
+    assert dfs.workspace_size(c) == 0
+
+
+def test_config_rule_allowed_edges():
+    assert dfs.validate_config(cfg_of(2, block_size=2)) == OK
+    assert dfs.validate_config(cfg_of(2, block_size=64)) == OK
+    assert dfs.validate_config(cfg_of(2, top_k=64)) == OK
+    assert dfs.validate_config(cfg_of(2, conv_kernel_size=1)) == OK
+    assert dfs.validate_config(cfg_of(2, conv_kernel_size=4)) == OK
+    assert dfs.validate_config(cfg_of(2, vocab=16)) == OK
+    assert dfs.validate_config(cfg_of(0, hidden=16384, conv_group_size=16)) == OK  # fp32 has no LDS-resident head
+    assert dfs.validate_config(cfg_of(2, batch=8192, block_size=8)) == OK
+    assert dfs.validate_config(cfg_of(2, batch=8193, block_size=8)) == SHAPE
+
+
+def test_workspace_grows_with_shape():
+    small = dfs.workspace_size(cfg_of(2))
+    big = dfs.workspace_size(cfg_of(3))
+    assert big > small > 0
+    # K > 16 on bf16 and every fp32 shape keep the logits in the workspace
+    assert dfs.workspace_size(cfg_of(2, top_k=17)) >= 8 * 248320 * 4
+
+
+L = dfs.lib()
+
+
+def call(name, *args):
+    return getattr(L, name)(*args)
+
+
+def conv_args(cfg, h=A, wg=A, y=A, yf=None):
+    return (C.byref(cfg), h, wg, y, yf, None)
+
+
+def test_conv_validation():
+    c = cfg_of(2)
+    assert L.dfs_conv(None, A, A, A, None, None) == NULL
+    assert call("dfs_conv", *conv_args(c, h=None)) == NULL
+    assert call("dfs_conv", *conv_args(c, wg=None)) == NULL
+    assert call("dfs_conv", *conv_args(c, y=None)) == NULL
+    assert call("dfs_conv", *conv_args(c, h=A + 8)) == MISAL
+    assert call("dfs_conv", *conv_args(c, yf=A + 4)) == MISAL
+    assert call("dfs_conv", *conv_args(cfg_of(2, conv_kernel_size=3))) == UNSUP
+    assert call("dfs_conv", *conv_args(cfg_of(2, hidden=100))) == SHAPE
+
+
+def test_head_topk_validation():
+    c = cfg_of(2)
+    ws = dfs.workspace_size(c)
+    base = [C.byref(c), A, A, A, A, A, None, A, ws, None]
+
+    def with_(i, v):
+        a = list(base)
+        a[i] = v
+        return a
+
+    for i in (1, 2, 3, 4, 5, 7):
+        assert L.dfs_head_topk(*with_(i, None)) == NULL, i
+    for i in (1, 2, 3, 4, 5, 6):
+        assert L.dfs_head_topk(*with_(i, A + 8)) == MISAL, i
+    assert L.dfs_head_topk(*with_(7, A + 64)) == MISAL  # workspace wants 256 B
+    assert L.dfs_head_topk(*with_(8, ws - 1)) == WS
+    assert L.dfs_head_topk(*with_(0, C.byref(cfg_of(2, top_k=0)))) == SHAPE
+
+
+def test_topk_logits_validation():
+    c = cfg_of(1)
+    ws = dfs.workspace_size(c)
+    assert L.dfs_topk_logits(C.byref(c), None, A, A, A, A, ws, None) == NULL
+    assert L.dfs_topk_logits(C.byref(c), A, A, A + 4, A, A, ws, None) == MISAL
+    assert L.dfs_topk_logits(C.byref(c), A, A, A, A, A, 0, None) == WS
+    assert L.dfs_topk_logits(C.byref(cfg_of(1, vocab=3)), A, A, A, A, A, ws, None) == SHAPE
+
+
+def test_select_validation():
+    c = cfg_of(3)
+    ws = dfs.workspace_size(c)
+    base = [C.byref(c), A, A, A, A, A, A, A, None, A, ws, None]
+    for i in (1, 2, 3, 4, 5, 6, 7, 9):
+        a = list(base)
+        a[i] = None
+        assert L.dfs_select(*a) == NULL, i
+    for i in (1, 2, 3, 4, 5, 6, 7, 8):
+        a = list(base)
+        a[i] = A + 8
+        assert L.dfs_select(*a) == MISAL, i
+    a = list(base)
+    a[10] = 16
+    assert L.dfs_select(*a) == WS
+
+
+def test_draft_block_validation():
+    c = cfg_of(2)
+    ws = dfs.workspace_size(c)
+    base = [C.byref(c), A, A, A, A, A, A, A, A, None, None, A, ws, None]
+    for i in (1, 2, 3, 4, 5, 6, 7, 8, 11):
+        a = list(base)
+        a[i] = None
+        assert L.dfs_draft_block(*a) == NULL, i
+    for i in (1, 2, 3, 4, 5, 6, 7, 8, 9, 10):
+        a = list(base)
+        a[i] = A + 2
+        assert L.dfs_draft_block(*a) == MISAL, i
+    a = list(base)
+    a[12] = ws // 2
+    assert L.dfs_draft_block(*a) == WS
+    assert L.dfs_draft_block(C.byref(cfg_of(2, block_size=1)), *base[1:]) == SHAPE
+
+
+def test_binding_raises_typed_error():
+    c = cfg_of(2, block_size=1)
+    with pytest.raises(dfs.DFSError) as e:
+        dfs.conv(c, A, A, A, stream=0)
+    assert e.value.status == SHAPE and "DFS_ERR_SHAPE" in str(e.value)
