@@ -14,8 +14,10 @@ LIB = os.path.join(HERE, "libdflash2.so")
 SOURCES = ["conv.hip", "head.hip", "select.hip", "api.cpp"]
 ARCH = os.environ.get("DFS_OFFLOAD_ARCH", "gfx950")
 
-# Packed fp32 ops are switched off for all device code.
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+# Packed fp32 ops are switched off for all device code.  Code object v5 is
+# what the HIP runtime bundled with PyTorch loads; in a PyTorch process the
+# library binds to that runtime (see dflash2.py).
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 
@@ -39,7 +41,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", "-o", LIB + ".tmp",
+           *objs]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)

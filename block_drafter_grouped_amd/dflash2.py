@@ -53,6 +53,14 @@ class DFSError(RuntimeError):
 
 
 def _load():
+    # PyTorch ships its own HIP runtime with the same soname as the system
+    # one.  Importing torch first makes the dynamic loader bind this library
+    # to that already-loaded runtime; loading the library first would put two
+    # HIP runtimes in one process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python block_drafter_grouped_amd/build.py`")
     lib_ = C.CDLL(LIB_PATH)
