@@ -1,0 +1,211 @@
+"""Benchmark of the DFlash2 draft-block hot path on one MI355X.
+
+A step is one dfs_draft_block call: grouped causal conv, vocabulary head,
+log-softmax, per-slot top-K, transition scores and the Viterbi walk, over one
+batch of synthetic inputs already resident in HBM.  The default workload is
+the page drafter shape at batch 1 (hidden 5120, vocab 248 320, block 8, K 16,
+rank 256).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "draft blocks/sec & µs/block (conv+head+top-K+select), % HBM/MFMA roofline"
+
+WORKLOAD_NAMES = {
+    0: "tiny oracle check (batch 1, B 4, D 64, V 1000, K 4, r 16, fp32)",
+    1: "small drafter shape (batch 1, B 8, D 2560, V 151936, K 16, r 256, bf16)",
+    2: "page drafter shape, batch 1 (B 8, D 5120, V 248320, K 16, r 256, bf16)",
+    3: "page drafter shape, batch 32 (B 8, D 5120, V 248320, K 16, r 256, bf16)",
+    4: "long block, batch 8 (B 16, D 5120, V 248320, K 16, r 256, bf16)",
+}
+
+
+def head_stage_bytes(s) -> int:
+    """Algorithmic bytes of the lm_head + top-K stage: the weight once, the
+    conv output once, the candidates and lse out."""
+    esz = 2 if s.dtype == "bf16" else 4
+    return s.vocab * s.hidden * esz + s.rows * s.hidden * esz + s.rows * s.top_k * 8 + s.rows * 4
+
+
+def block_bytes(s) -> int:
+    """Algorithmic bytes of a whole draft block: conv (h in, generator, y
+    out), the head stage, and the gathered selector rows."""
+    esz = 2 if s.dtype == "bf16" else 4
+    conv = s.rows * s.hidden * esz * 2 + s.groups * s.ksize * s.hidden * esz
+    sel = s.batch * ((1 + s.top_k * (s.block - 2)) + s.top_k * (s.block - 1)) * s.rank * esz
+    return conv + head_stage_bytes(s) + sel
+
+
+def head_flops(s) -> int:
+    return 2 * s.rows * s.hidden * s.vocab
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(s, inp, budget_s: float) -> dict:
+    """The oracle, as it is, on the host cores: whole draft blocks of the
+    same workload until about budget_s seconds have passed (at least one)."""
+    import oracle
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.draft_block(s, inp["h"], inp["anchor"], inp["wg"], inp["W"], inp["P"], inp["Q"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    blocks = n * s.batch
+    return {"value": blocks / el, "unit": "blocks/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{n} full call(s) of the same workload ({blocks} blocks) in {el:.1f} s; CPU: {cpu_model()}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(wl.CONFIGS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline (0: skip)")
+    ap.add_argument("--stage-steps", type=int, default=None, help="calls per stage timing loop")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run 4 plain 1 GiB device copies (counter calibration for profiles)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: the draft-block path runs on one GPU; a run across several GPUs is not "
+              "implemented. Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import block_drafter_grouped_amd as dfs
+
+    s = wl.shape_of(args.workload)
+    inp = wl.make_inputs(args.workload)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+    h, W, P, Q, anchor = (dev(inp[k]) for k in ("h", "W", "P", "Q", "anchor"))
+    wg_cm = dev(np.ascontiguousarray(inp["wg"].T))
+    cfg = dfs.Config.of(s)
+    ws = torch.empty(dfs.workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    tdt = torch.int16 if s.dtype == "bf16" else torch.float32
+    path = torch.empty((s.batch, s.block), dtype=torch.int32, device="cuda")
+    score = torch.empty((s.batch,), dtype=torch.float32, device="cuda")
+    ids = torch.empty((s.rows, s.top_k), dtype=torch.int32, device="cuda")
+    lp = torch.empty((s.rows, s.top_k), dtype=torch.float32, device="cuda")
+    lse = torch.empty((s.rows,), dtype=torch.float32, device="cuda")
+    y = torch.empty((s.rows, s.hidden), dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dfs.draft_block(cfg, h, anchor, wg_cm, W, P, Q, path, score, ws, cand_ids=ids, cand_logp=lp,
+                        stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # Per-stage split, each stage timed alone with HIP events on the same stream.
+    n_stage = args.stage_steps or args.steps
+
+    def timed(fn) -> float:
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n_stage):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n_stage * 1e3  # us
+
+    us_conv = timed(lambda: dfs.conv(cfg, h, wg_cm, y, stream=stream))
+    us_head = timed(lambda: dfs.head_topk(cfg, y, W, ids, lp, lse, ws, stream=stream))
+    us_sel = timed(lambda: dfs.select(cfg, anchor, ids, lp, P, Q, path, score, ws, stream=stream))
+
+    hb = head_stage_bytes(s)
+    achieved = hb / (us_head * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "lm_head + top-K stage (head_bf16_kernel + merge_kernel, one dfs_head_topk call)",
+            "bytes_per_launch": hb, "us_per_launch": round(us_head, 2)}
+    if s.dtype != "bf16":
+        roof["bound"] = "latency"
+
+    out = {
+        "metric": METRIC,
+        "value": round(s.batch / (ms_step * 1e-3), 2),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Philox normals: h~N(0,1), Wg~N(0,1/D), W~N(0,9/D), P,Q~N(0,1/r))",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": s.batch, "block": s.block,
+                   "hidden": s.hidden, "vocab": s.vocab, "top_k": s.top_k, "rank": s.rank,
+                   "conv_group_size": s.group, "conv_kernel_size": s.ksize, "parallelism": "none (1 GPU)"},
+        "us_per_block": round(ms_step * 1e3 / s.batch, 3),
+        "stage_us": {"conv": round(us_conv, 2), "head_topk": round(us_head, 2), "select": round(us_sel, 2)},
+        "block_hbm_frac": round(block_bytes(s) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "head_mfma_frac": round(head_flops(s) / (us_head * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if args.copy_probe:
+        # A plain copy of known size: HBM counters of a profiled run divided
+        # by 1 GiB read + 1 GiB written give the counters' scale.
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(s, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
