@@ -155,7 +155,7 @@ def main() -> int:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n_stage * 1e3  # us
 
-    us_conv = timed(lambda: dfs.conv(cfg, h, wg_cm, y, stream=stream))
+    us_conv = timed(lambda: dfs.conv(cfg, h, wg_cm, y, ws, stream=stream))
     us_head = timed(lambda: dfs.head_topk(cfg, y, W, ids, lp, lse, ws, stream=stream))
     us_sel = timed(lambda: dfs.select(cfg, anchor, ids, lp, P, Q, path, score, ws, stream=stream))
 
@@ -163,7 +163,7 @@ def main() -> int:
     achieved = hb / (us_head * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "lm_head + top-K stage (head_bf16_kernel + merge_kernel, one dfs_head_topk call)",
+            "kernel": "lm_head + top-K stage (head_pair_kernel + merge_kernel, one dfs_head_topk call)",
             "bytes_per_launch": hb, "us_per_launch": round(us_head, 2)}
     if s.dtype != "bf16":
         roof["bound"] = "latency"

@@ -74,13 +74,15 @@ size_t dfs_workspace_size(const dfs_config* cfg) {
     return dfs::ws_layout(dims_of(cfg)).total;
 }
 
-int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm, void* y, float* y_f32, void* stream) {
+int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm, void* y, float* y_f32, void* ws,
+             size_t ws_bytes, void* stream) {
     int st = check_cfg(cfg);
     if (st) return st;
     if (!h || !wg_cm || !y) return DFS_ERR_NULL;
     if (misaligned(h, 16) || misaligned(wg_cm, 16) || misaligned(y, 16) || misaligned(y_f32, 16))
         return DFS_ERR_MISALIGNED;
-    return hip_status(dfs::launch_conv(dims_of(cfg), h, wg_cm, y, y_f32, (hipStream_t)stream));
+    if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+    return hip_status(dfs::launch_conv(dims_of(cfg), h, wg_cm, y, y_f32, (char*)ws, (hipStream_t)stream));
 }
 
 int dfs_head_topk(const dfs_config* cfg, const void* y, const void* W, int32_t* cand_ids, float* cand_logp,
@@ -141,7 +143,7 @@ int dfs_draft_block(const dfs_config* cfg, const void* h, const int32_t* anchor,
     int32_t* cids = cand_ids ? cand_ids : (int32_t*)(w + L.cids);
     float* clogp = cand_logp ? cand_logp : (float*)(w + L.clogp);
     float* lse = (float*)(w + L.lse);
-    if ((st = hip_status(dfs::launch_conv(d, h, wg_cm, y, nullptr, s)))) return st;
+    if ((st = hip_status(dfs::launch_conv(d, h, wg_cm, y, nullptr, w, s)))) return st;
     if ((st = hip_status(dfs::launch_head_topk(d, y, W, cids, clogp, lse, nullptr, w, s)))) return st;
     return hip_status(dfs::launch_select(d, anchor, cids, clogp, P, Q, path, path_score, nullptr, w, s));
 }

@@ -8,6 +8,7 @@ namespace dfs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -45,20 +46,56 @@ __device__ __forceinline__ float key_value(uint64_t k) {
 }
 __device__ __forceinline__ int32_t key_id(uint64_t k) { return (int32_t)(0xFFFFFFFFu - (uint32_t)k); }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-    lo = (uint32_t)__shfl_xor((int)lo, m, kWave);
-    hi = (uint32_t)__shfl_xor((int)hi, m, kWave);
-    return ((uint64_t)hi << 32) | lo;
+// ---------------------------------------------------------------------------
+// Wave-wide reductions.  Four DPP steps (quad swaps, then the half-row and
+// row mirrors) make every lane of each 16-lane row hold the row's result;
+// v_readlane then brings the four row results to scalar registers.  DPP moves
+// are VALU operations with a few cycles of latency, where an LDS-routed
+// shuffle costs a full LDS round trip per step.  All 64 lanes must be active.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    return ((uint64_t)dpp_u32<CTRL>((uint32_t)(x >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)x);
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+}
+__device__ __forceinline__ float readlane_f32(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        uint64_t y = shfl_xor_u64(x, m);
-        x = y > x ? y : x;
-    }
-    return x;
+    x = umax64(x, dpp_u64<kDppQuadXor1>(x));
+    x = umax64(x, dpp_u64<kDppQuadXor2>(x));
+    x = umax64(x, dpp_u64<kDppHalfMirror>(x));
+    x = umax64(x, dpp_u64<kDppMirror>(x));
+    return umax64(umax64(readlane_u64(x, 0), readlane_u64(x, 16)), umax64(readlane_u64(x, 32), readlane_u64(x, 48)));
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+    x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_f32<kDppMirror>(x));
+    return fmaxf(fmaxf(readlane_f32(x, 0), readlane_f32(x, 16)), fmaxf(readlane_f32(x, 32), readlane_f32(x, 48)));
 }
 
 // Online (max, sum of exp) pair: value set {x} is represented by
@@ -74,15 +111,85 @@ __device__ __forceinline__ MaxSum ms_combine(MaxSum a, MaxSum b) {
     return MaxSum{m, a.s * __expf(a.m - m) + b.s * __expf(b.m - m)};
 }
 
-// Fixed butterfly order: identical results from run to run.
-__device__ __forceinline__ MaxSum wave_ms_reduce(MaxSum a) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        MaxSum b{__shfl_xor(a.m, m, kWave), __shfl_xor(a.s, m, kWave)};
-        a = ms_combine(a, b);
-    }
-    return a;
+template <int CTRL>
+__device__ __forceinline__ MaxSum ms_dpp_step(MaxSum a) {
+    return ms_combine(a, MaxSum{dpp_f32<CTRL>(a.m), dpp_f32<CTRL>(a.s)});
 }
+
+// Fixed combination order: identical results from run to run.
+__device__ __forceinline__ MaxSum wave_ms_reduce(MaxSum a) {
+    a = ms_dpp_step<kDppQuadXor1>(a);
+    a = ms_dpp_step<kDppQuadXor2>(a);
+    a = ms_dpp_step<kDppHalfMirror>(a);
+    a = ms_dpp_step<kDppMirror>(a);
+    MaxSum r = MaxSum{readlane_f32(a.m, 0), readlane_f32(a.s, 0)};
+    r = ms_combine(r, MaxSum{readlane_f32(a.m, 16), readlane_f32(a.s, 16)});
+    r = ms_combine(r, MaxSum{readlane_f32(a.m, 32), readlane_f32(a.s, 32)});
+    r = ms_combine(r, MaxSum{readlane_f32(a.m, 48), readlane_f32(a.s, 48)});
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Merging sorted key lists across lanes.  Each lane holds N keys sorted
+// descending.  One level takes a partner lane's list (a DPP move), keeps the
+// element-wise max of the own list and the partner's list reversed -- which
+// holds exactly the N largest of the union, as a bitonic sequence -- and sorts
+// that with a bitonic half-cleaner cascade.  Six levels (quad swaps, the two
+// mirrors, then the row broadcasts into rows 1/3 and row 3) leave in lane 63
+// the N largest keys of all 64 lanes.  All lanes must be active.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64m(uint64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(x >> 32), CTRL, ROW_MASK, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int N>
+__device__ __forceinline__ void bitonic_clean_desc(uint64_t (&c)[N]) {
+#pragma unroll
+    for (int st = N / 2; st >= 1; st >>= 1) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if ((i & st) == 0) {
+                const uint64_t x = c[i], y = c[i + st];
+                const bool gt = x > y;
+                c[i] = gt ? x : y;
+                c[i + st] = gt ? y : x;
+            }
+        }
+    }
+}
+
+// a <- the N largest keys of a and b (both sorted descending), sorted.
+template <int N>
+__device__ __forceinline__ void merge_top(uint64_t (&a)[N], const uint64_t (&b)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = umax64(a[i], b[N - 1 - i]);
+    bitonic_clean_desc<N>(a);
+}
+
+template <int CTRL, int ROW_MASK, int N>
+__device__ __forceinline__ void merge_top_dpp(uint64_t (&a)[N]) {
+    uint64_t b[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) b[i] = dpp_u64m<CTRL, ROW_MASK>(a[i]);
+    merge_top<N>(a, b);
+}
+
+template <int N>
+__device__ __forceinline__ void wave_merge_top(uint64_t (&a)[N]) {
+    merge_top_dpp<kDppQuadXor1, 0xF>(a);
+    merge_top_dpp<kDppQuadXor2, 0xF>(a);
+    merge_top_dpp<kDppHalfMirror, 0xF>(a);
+    merge_top_dpp<kDppMirror, 0xF>(a);
+    merge_top_dpp<kDppRowBcast15, 0xA>(a);
+    merge_top_dpp<kDppRowBcast31, 0x8>(a);
+}
+
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+constexpr int kCandCap = 256;
 
 // Sorted (descending) register list of KL keys; inserts x, dropping the
 // smallest.  Straight-line code so the list stays in registers.
@@ -102,14 +209,14 @@ __device__ __forceinline__ void list_insert(uint64_t (&lst)[KL], uint64_t x) {
 // round takes the largest head; keys are distinct, so exactly one lane
 // advances.  Empty heads read as 0.
 __device__ __forceinline__ void wave_tournament(const uint64_t* lists, int nsrc, int stride, int len,
-                                                int K, uint64_t* out) {
+                                                int K, uint64_t* out, int out_stride = 1) {
     const int lane = threadIdx.x & (kWave - 1);
     int head = 0;
     for (int round = 0; round < K; ++round) {
         uint64_t key = (lane < nsrc && head < len) ? lists[lane * stride + head] : 0ull;
         uint64_t mx = wave_max_u64(key);
         if (key == mx && mx != 0ull) ++head;
-        if (lane == 0) out[round] = mx;
+        if (lane == 0) out[(size_t)round * out_stride] = mx;
     }
 }
 

@@ -10,10 +10,7 @@
 // bf16: the generator is a dense [rows, D] x [D, G*ks] contraction and runs
 // on MFMA (v_mfma_f32_16x16x32_bf16).  Both operands are K-contiguous in HBM
 // (h row-major, the generator channel-major), so every lane loads 16 B
-// straight into its MFMA operand registers.  A workgroup owns a 16-column x
-// 64-row tile of z; its waves split D and sum their partial tiles in LDS in a
-// fixed order, then the same workgroup applies the softmax and the causal
-// taps for the 16/ks groups its columns cover.  fp32: a plain VALU kernel.
+// straight into its MFMA operand registers.  fp32: a plain VALU kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,65 +18,103 @@ namespace dfs {
 
 namespace {
 
-constexpr int kConvRows = 64;  // rows per workgroup tile (4 MFMA fragments)
-constexpr int kConvWaves = 8;  // waves splitting the D reduction
+// The generator reads the whole [G*ks, D] weight (6.5 MB at the page shape)
+// for only a few rows, so a per-column-tile workgroup would leave most CUs
+// idle and be bound by per-CU bandwidth.  The D reduction is therefore split
+// over kConvSplit workgroups per tile, whose partial tiles go to the
+// workspace; a second kernel sums them in a fixed order, applies the tap
+// softmax and the causal taps.
+constexpr int kConvSplit = 8;
+constexpr int kGenWaves = 4;
 
-template <int NWK>
-__global__ __launch_bounds__(NWK * kWave) void conv_bf16_kernel(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ wg, uint16_t* __restrict__ y,
-    float* __restrict__ y_f32, int rows, int B, int D, int gs, int ks, int C) {
-    __shared__ float red[NWK][4][4][kWave];
-    __shared__ float zt[kConvRows][17];
-    __shared__ float wt[kConvRows][17];
-
+// NF MFMA row fragments (16 rows each) per workgroup.  Each wave puts the
+// loads of G k-steps in flight together.
+template <int NF, int G>
+__global__ __launch_bounds__(kGenWaves * kWave) void conv_gen_kernel(const uint16_t* __restrict__ h,
+                                                                   const uint16_t* __restrict__ wg,
+                                                                   float* __restrict__ zpart, int rows, int D,
+                                                                   int C) {
+    __shared__ float red[kGenWaves][NF][4][kWave];
     const int col0 = blockIdx.x * 16;
-    const int row0 = blockIdx.y * kConvRows;
+    const int row0 = blockIdx.y * 16 * NF;
+    const int split = blockIdx.z;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int i16 = lane & 15, q = lane >> 4;
-    const int nf = min(4, (rows - row0 + 15) / 16);
+    const int nf = min(NF, (rows - row0 + 15) / 16);
     const int S = D / 32;
-    const int s_beg = (int)((int64_t)S * wave / NWK), s_end = (int)((int64_t)S * (wave + 1) / NWK);
+    const int w_beg = (int)((int64_t)S * split / kConvSplit), w_end = (int)((int64_t)S * (split + 1) / kConvSplit);
+    const int s_beg = w_beg + (w_end - w_beg) * wave / kGenWaves;
+    const int s_end = w_beg + (w_end - w_beg) * (wave + 1) / kGenWaves;
 
     // MFMA operands: A = generator rows (i = column of z), B = hidden rows
-    // (j = row of z); lane holds 8 consecutive channels of one row.
+    // (j = row of z); each lane loads 8 consecutive channels of one row.
     const uint16_t* arow = wg + (size_t)min(col0 + i16, C - 1) * D + 8 * q;
-    const uint16_t* brow[4];
+    const uint16_t* brow[NF];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) brow[f] = h + (size_t)min(row0 + 16 * f + i16, rows - 1) * D + 8 * q;
+    for (int f = 0; f < NF; ++f) brow[f] = h + (size_t)min(row0 + 16 * f + i16, rows - 1) * D + 8 * q;
 
-    f32x4 acc[4];
+    f32x4 acc[NF];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = s_beg; s < s_end; ++s) {
-        const bf16x8 a = *(const bf16x8*)(arow + 32 * s);
+    for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = s_beg; s0 < s_end; s0 += G) {
+        bf16x8 av[G], bv[G][NF];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            if (f < nf) {
-                const bf16x8 b = *(const bf16x8*)(brow[f] + 32 * s);
-                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+        for (int u = 0; u < G; ++u) {
+            const int s = min(s0 + u, s_end - 1);
+            av[u] = *(const bf16x8*)(arow + 32 * s);
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+                if (f < nf) bv[u][f] = *(const bf16x8*)(brow[f] + 32 * s);
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            if (s0 + u < s_end) {
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+                    if (f < nf) acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][f], acc[f], 0, 0, 0);
             }
         }
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[wave][f][r][lane] = acc[f][r];
     __syncthreads();
-
-    // Sum the D-split partials in wave order; MFMA output lane l, register r
-    // holds z[col 4*(l/16) + r][row l%16] of its fragment.
-    for (int e = threadIdx.x; e < 4 * 4 * kWave; e += NWK * kWave) {
+    // Sum the waves in order; MFMA output lane l, register r holds
+    // z[col 4*(l/16) + r][row l%16] of its fragment.
+    for (int e = threadIdx.x; e < NF * 4 * kWave; e += kGenWaves * kWave) {
         const int f = e / (4 * kWave), r = (e / kWave) & 3, ln = e & (kWave - 1);
+        const int row = row0 + 16 * f + (ln & 15), col = col0 + 4 * (ln >> 4) + r;
+        if (row >= rows || col >= C) continue;
         float sum = 0.f;
-        for (int w = 0; w < NWK; ++w) sum += red[w][f][r][ln];
-        zt[16 * f + (ln & 15)][4 * (ln >> 4) + r] = sum;
+#pragma unroll
+        for (int w = 0; w < kGenWaves; ++w) sum += red[w][f][r][ln];
+        zpart[((size_t)split * rows + row) * C + col] = sum;
+    }
+}
+
+// Sums the split partials of a 16-column x 16-row tile of z in split order,
+// applies the softmax over each group's taps, then the causal taps to the
+// 16/ks groups the columns cover.
+__global__ __launch_bounds__(256) void conv_apply_kernel(const uint16_t* __restrict__ h,
+                                                         const float* __restrict__ zpart, uint16_t* __restrict__ y,
+                                                         float* __restrict__ y_f32, int rows, int B, int D, int gs,
+                                                         int ks, int C) {
+    __shared__ float zt[16][17];
+    __shared__ float wt[16][17];
+    const int col0 = blockIdx.x * 16, row0 = blockIdx.y * 16;
+    const int t0 = threadIdx.x;
+    {
+        const int rr = t0 / 16, cc = t0 % 16, row = row0 + rr, col = col0 + cc;
+        float z = 0.f;
+        if (row < rows && col < C)
+            for (int k = 0; k < kConvSplit; ++k) z += zpart[((size_t)k * rows + row) * C + col];
+        zt[rr][cc] = z;
     }
     __syncthreads();
-
     const int ncol = min(16, C - col0);  // a multiple of ks
     const int ng = ncol / ks;
-    for (int e = threadIdx.x; e < kConvRows * ng; e += NWK * kWave) {
+    for (int e = t0; e < 16 * ng; e += blockDim.x) {
         const int rr = e / ng, gl = e % ng;
         float m = -INFINITY;
         for (int j = 0; j < ks; ++j) m = fmaxf(m, zt[rr][gl * ks + j]);
@@ -91,10 +126,9 @@ __global__ __launch_bounds__(NWK * kWave) void conv_bf16_kernel(
         for (int j = 0; j < ks; ++j) wt[rr][gl * ks + j] = ex[j] / den;
     }
     __syncthreads();
-
     const int c0 = (col0 / ks) * gs;
     const int nch = ng * gs;
-    for (int e = threadIdx.x; e < kConvRows * nch; e += NWK * kWave) {
+    for (int e = t0; e < 16 * nch; e += blockDim.x) {
         const int rr = e / nch, cc = e % nch;
         const int row = row0 + rr;
         if (row >= rows) continue;
@@ -139,12 +173,29 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32, hipStream_t s) {
+size_t conv_ws_bytes(const Dims& d) {
+    return d.bf16 ? (size_t)kConvSplit * d.rows() * d.taps() * sizeof(float) : 0;
+}
+
+hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32, char* ws,
+                       hipStream_t s) {
     const int C = d.taps();
     if (d.bf16) {
-        dim3 grid((C + 15) / 16, (d.rows() + kConvRows - 1) / kConvRows);
-        conv_bf16_kernel<kConvWaves><<<grid, kConvWaves * kWave, 0, s>>>(
-            (const uint16_t*)h, (const uint16_t*)wg_cm, (uint16_t*)y, y_f32, d.rows(), d.B, d.D, d.gs, d.ks, C);
+        float* zpart = (float*)(ws + ws_layout(d).zpart);
+        if (d.rows() <= 16) {
+            dim3 grid((C + 15) / 16, 1, kConvSplit);
+            conv_gen_kernel<1, 8><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
+                                                                    zpart, d.rows(), d.D, C);
+        } else {
+            dim3 grid((C + 15) / 16, (d.rows() + 63) / 64, kConvSplit);
+            conv_gen_kernel<4, 4><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
+                                                                    zpart, d.rows(), d.D, C);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dim3 grid2((C + 15) / 16, (d.rows() + 15) / 16);
+        conv_apply_kernel<<<grid2, 256, 0, s>>>((const uint16_t*)h, zpart, (uint16_t*)y, y_f32, d.rows(), d.B, d.D,
+                                                d.gs, d.ks, C);
     } else {
         conv_f32_kernel<<<d.rows(), 256, 2 * (size_t)C * sizeof(float), s>>>(
             (const float*)h, (const float*)wg_cm, (float*)y, y_f32, d.rows(), d.B, d.D, d.gs, d.ks, C);

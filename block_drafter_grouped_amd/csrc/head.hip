@@ -134,8 +134,148 @@ __global__ __launch_bounds__(NW * kWave) void head_bf16_kernel(
     }
     __syncthreads();
     for (int jr = wave; jr < rows; jr += NW) {
-        wave_tournament(L + (size_t)jr * NSRC * K, NSRC, K, K, K,
-                        part_keys + ((size_t)(row_base + jr) * nch + c) * K);
+        wave_tournament(L + (size_t)jr * NSRC * K, NSRC, K, K, K, part_keys + (size_t)(row_base + jr) * K * nch + c,
+                        nch);
+        MaxSum x{-INFINITY, 0.f};
+        if (lane < NSRC) {
+            const float2 p = M[jr * NSRC + lane];
+            x = MaxSum{p.x, p.y};
+        }
+        x = wave_ms_reduce(x);
+        if (lane == 0) part_ms[(size_t)(row_base + jr) * nch + c] = make_float2(x.m, x.s);
+    }
+}
+
+// Streaming head with whole-line loads.  The plain MFMA operand layout makes
+// every wave load 16 rows x 64 B; with non-temporal loads, reads of at least
+// 128 B per row per instruction stream markedly faster.  Here a tile is 8
+// vocabulary rows and a k-step covers 64 channels as two 32-channel segments
+// a and b: MFMA rows 0-7 carry segment a of the 8 rows and rows 8-15 carry
+// segment b, while B-operand columns 0-7 carry the hidden rows at segment a
+// and columns 8-15 the same rows at segment b.  The two diagonal 8x8 blocks
+// of the product then hold the two partial dot products, one lane shuffle
+// adds them, and each load instruction reads 8 rows x 128 contiguous bytes.
+template <int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
+    const uint16_t* __restrict__ y, int rows_total, int D, const uint16_t* __restrict__ W, int V, int nch, int K,
+    uint64_t* __restrict__ part_keys, float2* __restrict__ part_ms, float* __restrict__ logits) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int KL = 16;
+    constexpr int NSRC = NW * 2;  // two lanes per row per wave carry results
+    const int c = blockIdx.x;
+    const int row_base = blockIdx.y * kRowsPass;
+    const int rows = min(kRowsPass, rows_total - row_base);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int S = D / 64;
+    const int i16 = lane & 15, q = lane >> 4;
+
+    const int64_t T = ((int64_t)V + 7) / 8;
+    const int t_beg = (int)(T * c / nch), t_end = (int)(T * (c + 1) / nch);
+    const int my_n = (t_end - t_beg - wave + NW - 1) / NW;
+    const int GPT = S / U;
+    const int total = my_n * GPT;
+    const int a_off = 32 * (i16 >> 3) + 8 * q;
+
+    auto tile_ptr = [&](int i) -> const uint16_t* {
+        const int tt = t_beg + wave + i * NW;
+        const int v = min(tt * 8 + (i16 & 7), V - 1);
+        return W + (size_t)v * D + a_off;
+    };
+    auto ldw = [](const uint16_t* p) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)p));
+    };
+
+    // The first weight loads do not depend on the hidden rows: issue them
+    // before staging those.
+    bf16x8 a[U];
+    const uint16_t* cur = tile_ptr(0);
+    if (total > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = ldw(cur + 64 * u);
+    }
+
+    // Hidden rows -> LDS.  16-B unit (s, q, j): row j & 7, channels
+    // 64s + 32(j >> 3) + 8q .. +7, so the B operand of k-step s is one
+    // contiguous 1 KB read by the 64 lanes.
+    {
+        uint4* ys = (uint4*)smem;
+        for (int u = threadIdx.x; u < S * 64; u += NW * kWave) {
+            const int j = u & 15, qq = (u >> 4) & 3, s = u >> 6, row = j & 7;
+            uint4 v = {0u, 0u, 0u, 0u};
+            if (row < rows) v = *(const uint4*)(y + (size_t)(row_base + row) * D + 64 * s + 32 * (j >> 3) + 8 * qq);
+            ys[u] = v;
+        }
+    }
+    __syncthreads();
+    const uint4* ysb = (const uint4*)smem + q * 16 + i16;
+
+    uint64_t lst[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) lst[i] = 0ull;
+    MaxSum ms{-INFINITY, 0.f};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Lanes 0-7 and 16-23 own results: row i16, vocabulary 4q .. 4q+3 of the
+    // tile; their partner lane + 40 holds the segment-b half.
+    const bool owner = (i16 < 8) && (q < 2) && (i16 < rows);
+
+    int ti = 0, gi = 0;
+    for (int g = 0; g < total; ++g) {
+        int nti = ti, ngi = gi + 1;
+        if (ngi == GPT) {
+            ngi = 0;
+            nti = ti + 1;
+        }
+        const uint16_t* nxt = (g + 1 < total) ? (ngi == 0 ? tile_ptr(nti) : cur + 64 * U) : cur;
+        const int s0 = gi * U;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bf16x8 b = *(const bf16x8*)(ysb + (size_t)(s0 + u) * 64);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b, acc, 0, 0, 0);
+            a[u] = ldw(nxt + 64 * u);
+        }
+        if (ngi == 0) {
+            float v4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = acc[r] + __shfl(acc[r], (lane + 40) & (kWave - 1), kWave);
+            const int v0 = (t_beg + wave + ti * NW) * 8 + 4 * q;
+            if (owner) {
+                float mnew = ms.m;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (v0 + r < V) mnew = fmaxf(mnew, v4[r]);
+                float s = (ms.m == -INFINITY) ? 0.f : ms.s * __expf(ms.m - mnew);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (v0 + r < V) {
+                        s += __expf(v4[r] - mnew);
+                        const uint64_t key = make_key(v4[r], (uint32_t)(v0 + r));
+                        if (key > lst[KL - 1]) list_insert<KL>(lst, key);
+                        if (logits) logits[(size_t)(row_base + i16) * V + v0 + r] = v4[r];
+                    }
+                }
+                ms = MaxSum{mnew, s};
+            }
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        cur = nxt;
+        ti = nti;
+        gi = ngi;
+    }
+    __syncthreads();  // LDS switches from hidden rows to the merge lists
+
+    uint64_t* L = (uint64_t*)smem;                                     // [kRowsPass][NSRC][K]
+    float2* M = (float2*)(smem + (size_t)kRowsPass * NSRC * K * 8);  // [kRowsPass][NSRC]
+    if (owner) {
+        const int src = wave * 2 + q;
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+            if (i < K) L[((size_t)i16 * NSRC + src) * K + i] = lst[i];
+        M[i16 * NSRC + src] = make_float2(ms.m, ms.s);
+    }
+    __syncthreads();
+    for (int jr = wave; jr < rows; jr += NW) {
+        wave_tournament(L + (size_t)jr * NSRC * K, NSRC, K, K, K, part_keys + (size_t)(row_base + jr) * K * nch + c,
+                        nch);
         MaxSum x{-INFINITY, 0.f};
         if (lane < NSRC) {
             const float2 p = M[jr * NSRC + lane];
@@ -181,58 +321,182 @@ __global__ __launch_bounds__(kWave) void logits_partial_kernel(const float* __re
     for (int i = 0; i < KL; ++i)
         if (i < K) lsm[lane * K + i] = lst[i];
     __syncthreads();
-    wave_tournament(lsm, kWave, K, K, K, part_keys + ((size_t)row * nch + c) * K);
+    wave_tournament(lsm, kWave, K, K, K, part_keys + (size_t)row * K * nch + c, nch);
     ms = wave_ms_reduce(ms);
     if (lane == 0) part_ms[(size_t)row * nch + c] = make_float2(ms.m, ms.s);
 }
 
-// Chunk partials -> candidates.  One workgroup (4 waves) per row: each wave
-// merges up to 64 chunk lists, then wave 0 merges the 4 wave lists.
-// lse = M + log S with (M, S) the combined (max, sum of exp).
-__global__ __launch_bounds__(256) void merge_kernel(const uint64_t* __restrict__ part_keys,
-                                                    const float2* __restrict__ part_ms, int nch, int K,
-                                                    int32_t* __restrict__ cand_ids, float* __restrict__ cand_logp,
-                                                    float* __restrict__ lse_out) {
-    extern __shared__ uint64_t sk[];  // [nch][K] then [4][K]
+// Chunk partials -> candidates.  Partial keys are stored element-major,
+// [row][k][chunk], so that threads reading consecutive chunks coalesce.
+//  K <= 64: one workgroup (4 waves) per row: a K-round tournament per wave
+//    over its 64 chunk lists, then over the 4 wave lists.
+// lse = M + log S with (M, S) the combined (max, sum of exp), combined in a
+// fixed order.
+// K <= 16, nch <= 256: one workgroup of 1024 threads per row.  Thread t owns
+// keys 4*(t/256) .. +3 of chunk t%256 (coalesced loads).  A threshold theta
+// with at least 16 real keys >= theta is the minimum over 16 groups of 16
+// chunks of the group's largest chunk head; every key of the row's top K is
+// >= theta.  The keys >= theta (a few dozen for ordinary data) are gathered
+// in LDS and each is placed by its rank among them (keys are distinct).  If
+// more than kCandCap keys pass (massively tied logits), wave 0 merges all
+// the lists with bitonic levels instead.  Both give the exact top K.
+__global__ __launch_bounds__(1024) void merge16_kernel(const uint64_t* __restrict__ part_keys,
+                                                       const float2* __restrict__ part_ms, int nch, int K,
+                                                       int32_t* __restrict__ cand_ids, float* __restrict__ cand_logp,
+                                                       float* __restrict__ lse_out) {
+    __shared__ uint64_t gmax[16];
+    __shared__ uint64_t cand[kCandCap];
+    __shared__ uint64_t fin[16];
     __shared__ float2 wms[4];
-    __shared__ uint64_t fin[64];
+    __shared__ int cnt;
+    __shared__ uint64_t theta_sh;
+    __shared__ float z_sh;
+    const int row = blockIdx.x, t = threadIdx.x;
+    const int lane = t & (kWave - 1), wave = t / kWave;
+    const int c = t & 255, sub = t >> 8;
+    const uint64_t* base = part_keys + (size_t)row * K * nch;
+    uint64_t k4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = 4 * sub + e;
+        k4[e] = (c < nch && i < K) ? base[(size_t)i * nch + c] : 0ull;
+    }
+    if (t == 0) cnt = 0;
+    if (sub == 0) {  // waves 0-3 hold the chunk heads (key 0 of every chunk)
+        MaxSum x{-INFINITY, 0.f};
+        if (c < nch) {
+            const float2 p = part_ms[(size_t)row * nch + c];
+            x = MaxSum{p.x, p.y};
+        }
+        x = wave_ms_reduce(x);
+        if (lane == 0) wms[wave] = make_float2(x.m, x.s);
+        uint64_t h = k4[0];
+        h = umax64(h, dpp_u64<kDppQuadXor1>(h));
+        h = umax64(h, dpp_u64<kDppQuadXor2>(h));
+        h = umax64(h, dpp_u64<kDppHalfMirror>(h));
+        h = umax64(h, dpp_u64<kDppMirror>(h));
+        if ((lane & 15) == 0) gmax[wave * 4 + lane / 16] = h;
+    }
+    __syncthreads();
+    if (t == 0) {
+        uint64_t th = gmax[0];
+        for (int g = 1; g < 16; ++g) th = umin64(th, gmax[g]);
+        theta_sh = th;
+        MaxSum zz{-INFINITY, 0.f};
+        for (int w = 0; w < 4; ++w) zz = ms_combine(zz, MaxSum{wms[w].x, wms[w].y});
+        z_sh = (zz.m == -INFINITY) ? -INFINITY : zz.m + logf(zz.s);
+    }
+    __syncthreads();
+    const uint64_t theta = theta_sh;
+    bool pass[4];
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        pass[e] = k4[e] >= theta && k4[e] != 0ull;
+        mine += pass[e] ? 1 : 0;
+    }
+    // Slots: wave-aggregated offsets from ballots, one LDS atomic per wave.
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int before = 0, total = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint64_t bal = __ballot(pass[e]);
+        before += __popcll(bal & lt);
+        total += __popcll(bal);
+    }
+    int wbase = 0;
+    if (lane == 0 && total > 0) wbase = atomicAdd(&cnt, total);
+    wbase = __shfl(wbase, 0, kWave);
+    __syncthreads();
+    const int n = cnt;
+    if (n <= kCandCap) {
+        int p = wbase + before;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (pass[e]) cand[p++] = k4[e];
+        __syncthreads();
+        for (int i = t; i < n; i += blockDim.x) {
+            const uint64_t key = cand[i];
+            int rank = 0;
+            for (int j = 0; j < n; ++j) rank += cand[j] > key ? 1 : 0;
+            if (rank < K) fin[rank] = key;
+        }
+    } else if (wave == 0) {
+        uint64_t l4[4][16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int cc = lane + kWave * j;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) l4[j][i] = (cc < nch && i < K) ? base[(size_t)i * nch + cc] : 0ull;
+        }
+        merge_top<16>(l4[0], l4[1]);
+        merge_top<16>(l4[2], l4[3]);
+        merge_top<16>(l4[0], l4[2]);
+        wave_merge_top<16>(l4[0]);
+        if (lane == kWave - 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) fin[i] = l4[0][i];
+        }
+    }
+    __syncthreads();
+    const float z = z_sh;
+    if (t < K) {
+        const uint64_t key = fin[t];
+        cand_ids[(size_t)row * K + t] = key_id(key);
+        cand_logp[(size_t)row * K + t] = key_value(key) - z;
+    }
+    if (t == 0) lse_out[row] = z;
+}
+
+__global__ __launch_bounds__(256) void merge64_kernel(const uint64_t* __restrict__ part_keys,
+                                                      const float2* __restrict__ part_ms, int nch, int K,
+                                                      int32_t* __restrict__ cand_ids, float* __restrict__ cand_logp,
+                                                      float* __restrict__ lse_out) {
+    constexpr int KL = 64;
+    __shared__ uint64_t tops[4][KL + 1];
+    __shared__ uint64_t fin[KL];
+    __shared__ float2 wms[4];
     __shared__ float zsh;
-    const int row = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const uint64_t* src = part_keys + (size_t)row * nch * K;
-    for (int i = threadIdx.x; i < nch * K; i += blockDim.x) sk[i] = src[i];
+    const int row = blockIdx.x, t = threadIdx.x;
+    const int lane = t & (kWave - 1), wave = t / kWave;
+    const bool have = t < nch;
+    const uint64_t* src = part_keys + (size_t)row * K * nch + (have ? t : 0);
+    uint64_t lst[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) lst[i] = (have && i < K) ? src[(size_t)i * nch] : 0ull;
     MaxSum x{-INFINITY, 0.f};
-    for (int i = threadIdx.x; i < nch; i += blockDim.x) {
-        const float2 p = part_ms[(size_t)row * nch + i];
-        x = ms_combine(x, MaxSum{p.x, p.y});
+    if (have) {
+        const float2 p = part_ms[(size_t)row * nch + t];
+        x = MaxSum{p.x, p.y};
     }
     x = wave_ms_reduce(x);
     if (lane == 0) wms[wave] = make_float2(x.m, x.s);
+    for (int round = 0; round < K; ++round) {
+        const uint64_t mx = wave_max_u64(lst[0]);
+        if (lst[0] == mx && mx != 0ull) {
+#pragma unroll
+            for (int i = 0; i < KL - 1; ++i) lst[i] = lst[i + 1];
+            lst[KL - 1] = 0ull;
+        }
+        if (lane == 0) tops[wave][round] = mx;
+    }
     __syncthreads();
-    uint64_t* tops = sk + (size_t)nch * K;
-    const int first = wave * kWave;
-    const int n = max(0, min(kWave, nch - first));
-    wave_tournament(sk + (size_t)first * K, n, K, K, K, tops + wave * K);
-    __syncthreads();
-    if (wave == 0) wave_tournament(tops, 4, K, K, K, fin);
-    if (threadIdx.x == 0) {
-        MaxSum t{-INFINITY, 0.f};
-        for (int w = 0; w < 4; ++w) t = ms_combine(t, MaxSum{wms[w].x, wms[w].y});
-        zsh = (t.m == -INFINITY) ? -INFINITY : t.m + logf(t.s);
+    if (wave == 0) wave_tournament(&tops[0][0], 4, KL + 1, K, K, fin);
+    if (t == 0) {
+        MaxSum zz{-INFINITY, 0.f};
+        for (int w = 0; w < 4; ++w) zz = ms_combine(zz, MaxSum{wms[w].x, wms[w].y});
+        zsh = (zz.m == -INFINITY) ? -INFINITY : zz.m + logf(zz.s);
     }
     __syncthreads();
     const float z = zsh;
-    for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    for (int k = t; k < K; k += blockDim.x) {
         const uint64_t key = fin[k];
         cand_ids[(size_t)row * K + k] = key_id(key);
         cand_logp[(size_t)row * K + k] = key_value(key) - z;
     }
-    if (threadIdx.x == 0) lse_out[row] = z;
+    if (t == 0) lse_out[row] = z;
 }
 
-// Largest prefetch depth (k-steps of weight loads in flight per wave) that
-// divides the k-steps of a tile; 8 keeps the kernel inside 128 VGPRs, the
-// budget of 16 waves per CU.
 int pick_u(int S) {
     for (int u : {8, 4, 2, 1})
         if (S % u == 0) return u;
@@ -268,12 +532,42 @@ hipError_t launch_head_bf16_u(const Dims& d, int K, const void* y, const void* W
     }
 }
 
+template <int NW, int U>
+hipError_t launch_head_pair_t(const Dims& d, int K, const void* y, const void* W, int nch, uint64_t* keys,
+                              float2* ms, float* logits, hipStream_t s) {
+    const int S = d.D / 64;
+    size_t lds = (size_t)S * 64 * 16;
+    const size_t merge = (size_t)kRowsPass * NW * 2 * K * 8 + (size_t)kRowsPass * NW * 2 * 8;
+    lds = std::max(std::max(lds, merge), kMinHeadLds);
+    auto fn = head_pair_kernel<NW, U>;
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    dim3 grid(nch, (d.rows() + kRowsPass - 1) / kRowsPass);
+    fn<<<grid, NW * kWave, lds, s>>>((const uint16_t*)y, d.rows(), d.D, (const uint16_t*)W, d.V, nch, K, keys, ms,
+                                     logits);
+    return hipGetLastError();
+}
+
+// Weight stream of the head for rows <= 8 per pass.  The whole-line kernel
+// needs D % 64 == 0 and a k-step count divisible by its prefetch depth.
+hipError_t launch_head_stream(const Dims& d, int K, const void* y, const void* W, int nch, uint64_t* keys,
+                              float2* ms, float* logits, hipStream_t s) {
+    if (d.D % 64 == 0) {
+        const int S = d.D / 64;
+        if (S % 8 == 0) return launch_head_pair_t<8, 8>(d, K, y, W, nch, keys, ms, logits, s);
+        if (S % 4 == 0) return launch_head_pair_t<8, 4>(d, K, y, W, nch, keys, ms, logits, s);
+        if (S % 2 == 0) return launch_head_pair_t<8, 2>(d, K, y, W, nch, keys, ms, logits, s);
+        return launch_head_pair_t<8, 1>(d, K, y, W, nch, keys, ms, logits, s);
+    }
+    return launch_head_bf16_u<16, 16>(d, K, y, W, nch, keys, ms, logits, s);
+}
+
 hipError_t launch_merge(const Dims& d, int nch, const uint64_t* keys, const float2* ms, int32_t* cand_ids,
                         float* cand_logp, float* lse, hipStream_t s) {
-    const size_t lds = ((size_t)nch * d.K + 4 * (size_t)d.K) * 8;
-    hipError_t e = hipFuncSetAttribute((const void*)merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    merge_kernel<<<d.rows(), 256, lds, s>>>(keys, ms, nch, d.K, cand_ids, cand_logp, lse);
+    if (d.K <= 16)
+        merge16_kernel<<<d.rows(), 1024, 0, s>>>(keys, ms, nch, d.K, cand_ids, cand_logp, lse);
+    else
+        merge64_kernel<<<d.rows(), 256, 0, s>>>(keys, ms, nch, d.K, cand_ids, cand_logp, lse);
     return hipGetLastError();
 }
 
@@ -312,35 +606,41 @@ WsLayout ws_layout(const Dims& d) {
     L.cids = take(rows * K * 4);
     L.clogp = take(rows * K * 4);
     L.lse = take(rows * 4);
+    L.zpart = take(conv_ws_bytes(d));
     L.total = o;
     return L;
 }
 
-hipError_t launch_head_topk(const Dims& d, const void* y, const void* W, int32_t* cand_ids, float* cand_logp,
-                            float* lse, float* logits_f32, char* ws, hipStream_t s) {
+hipError_t launch_head_partials(const Dims& d, const void* y, const void* W, float* logits_f32, char* ws,
+                                hipStream_t s) {
     const WsLayout L = ws_layout(d);
     const int nch = head_chunks(d);
     uint64_t* keys = (uint64_t*)(ws + L.keys);
     float2* ms = (float2*)(ws + L.ms);
+    if (d.bf16 && d.K <= 16) return launch_head_stream(d, d.K, y, W, nch, keys, ms, logits_f32, s);
+    float* logits = logits_f32 ? logits_f32 : (float*)(ws + L.logits);
     hipError_t e;
-    if (d.bf16 && d.K <= 16) {
-        e = launch_head_bf16_u<16, 16>(d, d.K, y, W, nch, keys, ms, logits_f32, s);
-    } else if (d.bf16) {
+    if (d.bf16) {
         // K > 16: per-lane register lists of 64 keys would spill, so the
         // logits are written out and ranked by the logits top-K kernel, which
         // overwrites the (16-key) partials the head kernel leaves behind.
-        float* logits = logits_f32 ? logits_f32 : (float*)(ws + L.logits);
-        e = launch_head_bf16_u<16, 16>(d, 16, y, W, nch, keys, ms, logits, s);
-        if (e == hipSuccess) e = launch_logits_partials(d, logits, nch, keys, ms, s);
+        e = launch_head_stream(d, 16, y, W, nch, keys, ms, logits, s);
     } else {
-        float* logits = logits_f32 ? logits_f32 : (float*)(ws + L.logits);
         head_f32_kernel<<<(d.V + 255) / 256, 256, 0, s>>>((const float*)y, (const float*)W, logits, d.rows(), d.D,
                                                           d.V);
         e = hipGetLastError();
-        if (e == hipSuccess) e = launch_logits_partials(d, logits, nch, keys, ms, s);
     }
     if (e != hipSuccess) return e;
-    return launch_merge(d, nch, keys, ms, cand_ids, cand_logp, lse, s);
+    return launch_logits_partials(d, logits, nch, keys, ms, s);
+}
+
+hipError_t launch_head_topk(const Dims& d, const void* y, const void* W, int32_t* cand_ids, float* cand_logp,
+                            float* lse, float* logits_f32, char* ws, hipStream_t s) {
+    hipError_t e = launch_head_partials(d, y, W, logits_f32, ws, s);
+    if (e != hipSuccess) return e;
+    const WsLayout L = ws_layout(d);
+    return launch_merge(d, head_chunks(d), (const uint64_t*)(ws + L.keys), (const float2*)(ws + L.ms), cand_ids,
+                        cand_logp, lse, s);
 }
 
 hipError_t launch_topk_logits(const Dims& d, const float* logits, int32_t* cand_ids, float* cand_logp, float* lse,

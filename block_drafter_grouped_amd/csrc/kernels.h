@@ -24,11 +24,14 @@ int head_chunks(const Dims& d);
 
 // Workspace carve-up (byte offsets from the 256-B aligned base).
 struct WsLayout {
-    size_t y, keys, ms, logits, T, cids, clogp, lse, total;
+    size_t y, keys, ms, logits, T, cids, clogp, lse, zpart, total;
 };
 WsLayout ws_layout(const Dims& d);
 
-hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32,
+// Bytes of split-reduction partials the bf16 conv keeps in the workspace.
+size_t conv_ws_bytes(const Dims& d);
+
+hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32, char* ws,
                        hipStream_t s);
 
 // Head + top-K.  Uses ws.keys / ws.ms (and ws.logits for fp32 if logits_f32
@@ -36,6 +39,11 @@ hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y,
 hipError_t launch_head_topk(const Dims& d, const void* y, const void* W, int32_t* cand_ids,
                             float* cand_logp, float* lse, float* logits_f32, char* ws,
                             hipStream_t s);
+
+// The head's per-chunk partials only (no merge); used by the whole-block
+// path, whose final kernel merges them.
+hipError_t launch_head_partials(const Dims& d, const void* y, const void* W, float* logits_f32, char* ws,
+                                hipStream_t s);
 
 hipError_t launch_topk_logits(const Dims& d, const float* logits, int32_t* cand_ids, float* cand_logp,
                               float* lse, char* ws, hipStream_t s);

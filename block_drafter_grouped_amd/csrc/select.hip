@@ -6,6 +6,7 @@
 // starts from the last verified token, as in the vLLM release-note article,
 // section "two additions").  The context gate of the post is taken as 1.
 //
+// Fast path (bf16 tables, K <= 16): select_fused_kernel, below.  General path:
 // sel_dots: one workgroup per (draft slot, block) computes the K x K matrix
 //   T_t[j, k] = <P[c_{t-1, j}], Q[c_{t, k}]>   (c_0 = {anchor}: a 1 x K row)
 // from rows gathered out of P and Q, fp32 accumulation.
@@ -117,9 +118,7 @@ __global__ __launch_bounds__(kWave) void viterbi_kernel(const int32_t* __restric
         d = on ? best + lp : -INFINITY;
         if (on) bp[t * 64 + lane] = (uint8_t)bj;
     }
-    float mx = d;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
+    const float mx = wave_max_f32(d);
     const uint64_t ball = __ballot(on && d == mx);
     const int kb = __ffsll((unsigned long long)ball) - 1;
     __syncthreads();
@@ -136,11 +135,135 @@ __global__ __launch_bounds__(kWave) void viterbi_kernel(const int32_t* __restric
     }
 }
 
+// Transition scores and the walk of one block, from candidates already in
+// LDS: Cs[t][k] (ids) and Ls[t][k] (node scores) for t = 1..B-1, a valid
+// anchor, and a barrier between filling them and this call.  Every thread
+// of the workgroup calls it.  Wave w computes T_t for t = 1 + w, 1 + w + NWS,
+// ... as one 16x16 MFMA tile (A = P rows of the previous slot's candidates,
+// or of the anchor for t = 1; B = Q rows of this slot's candidates), with
+// every gather of a slot in flight at once; wave 0 then walks.
+template <int NWS>
+__device__ __forceinline__ void select_block_lds(int b, int a, const int32_t (*Cs)[16], const float (*Ls)[16],
+                                                 float (*Ts)[16][16], uint8_t (*bp)[16],
+                                                 const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
+                                                 int32_t* __restrict__ path, float* __restrict__ path_score,
+                                                 int32_t* __restrict__ path_idx, int B, int K, int r) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int i16 = lane & 15, q = lane >> 4, kk = min(i16, K - 1);
+    const int nks = r / 32;
+    for (int t = 1 + wave; t < B; t += NWS) {
+        const int pa = (t == 1) ? a : Cs[t - 1][kk];
+        const int qb = Cs[t][kk];
+        const uint16_t* pr = P + (size_t)pa * r + 8 * q;
+        const uint16_t* qr = Q + (size_t)qb * r + 8 * q;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < nks; s0 += 8) {
+            bf16x8 av[8], bv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = min(s0 + u, nks - 1);
+                av[u] = *(const bf16x8*)(pr + 32 * s);
+                bv[u] = *(const bf16x8*)(qr + 32 * s);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
+        }
+        // lane holds T_t[4q + rr][i16]
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) Ts[t - 1][4 * q + rr][i16] = acc[rr];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+
+    const bool on = lane < K;
+    float d = on ? Ls[1][lane] + Ts[0][0][lane] : -INFINITY;
+    for (int t = 2; t < B; ++t) {
+        float tc[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tc[j] = Ts[t - 1][j][lane & 15];
+        float best = -INFINITY;
+        int bj = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j < K) {
+                const float dj = readlane_f32(d, j);
+                const float c = dj + tc[j];
+                if (j == 0 || c > best) {
+                    best = c;
+                    bj = j;
+                }
+            }
+        }
+        d = on ? best + Ls[t][lane & 15] : -INFINITY;
+        if (on) bp[t][lane] = (uint8_t)bj;
+    }
+    const float mx = wave_max_f32(d);
+    const uint64_t ball = __ballot(on && d == mx);
+    const int kb = __ffsll((unsigned long long)ball) - 1;
+    if (lane == 0) {
+        int k = kb;
+        for (int t = B - 1; t >= 1; --t) {
+            path[(size_t)b * B + t] = Cs[t][k];
+            if (path_idx) path_idx[(size_t)b * B + t] = k;
+            if (t >= 2) k = bp[t][k];
+        }
+        path[(size_t)b * B] = a;
+        if (path_idx) path_idx[(size_t)b * B] = -1;
+        path_score[b] = mx;
+    }
+}
+
+__device__ __forceinline__ void write_bad_block(int b, int B, int32_t* path, float* path_score, int32_t* path_idx) {
+    for (int t = threadIdx.x; t < B; t += blockDim.x) {
+        path[(size_t)b * B + t] = -1;
+        if (path_idx) path_idx[(size_t)b * B + t] = -1;
+    }
+    if (threadIdx.x == 0) path_score[b] = __int_as_float(0x7FC00000);
+}
+
+// Selector for bf16 tables with K <= 16 and r % 32 == 0, on given candidates.
+template <int NWS>
+__global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
+    const int32_t* __restrict__ anchor, const int32_t* __restrict__ cand_ids, const float* __restrict__ cand_logp,
+    const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, int32_t* __restrict__ path,
+    float* __restrict__ path_score, int32_t* __restrict__ path_idx, int B, int K, int r, int V) {
+    extern __shared__ float Tsm[];  // [B-1][16][16]
+    __shared__ float Ls[64][16];
+    __shared__ int32_t Cs[64][16];
+    __shared__ uint8_t bp[64][16];
+    const int b = blockIdx.x, t0 = threadIdx.x;
+    const int a = anchor[b];
+    bool bad = (a < 0 || a >= V);
+    for (int i = t0; i < (B - 1) * K; i += NWS * kWave) {
+        const int t = 1 + i / K, k = i % K;
+        const int id = cand_ids[((size_t)b * B + t) * K + k];
+        bad |= (id < 0 || id >= V);
+        Cs[t][k] = id;
+        Ls[t][k] = cand_logp[((size_t)b * B + t) * K + k];
+    }
+    if (__syncthreads_or(bad)) {
+        write_bad_block(b, B, path, path_score, path_idx);
+        return;
+    }
+    select_block_lds<NWS>(b, a, Cs, Ls, (float(*)[16][16])Tsm, bp, P, Q, path, path_score, path_idx, B, K, r);
+}
+
 }  // namespace
 
 hipError_t launch_select(const Dims& d, const int32_t* anchor, const int32_t* cand_ids, const float* cand_logp,
                          const void* P, const void* Q, int32_t* path, float* path_score, int32_t* path_idx, char* ws,
                          hipStream_t s) {
+    if (d.bf16 && d.K <= 16 && d.r % 32 == 0) {
+        const size_t lds = (size_t)(d.B - 1) * 16 * 16 * sizeof(float);
+        hipError_t e = hipFuncSetAttribute((const void*)select_fused_kernel<8>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        select_fused_kernel<8><<<d.batch, 8 * kWave, lds, s>>>(anchor, cand_ids, cand_logp, (const uint16_t*)P,
+                                                             (const uint16_t*)Q, path, path_score, path_idx, d.B,
+                                                             d.K, d.r, d.V);
+        return hipGetLastError();
+    }
     const WsLayout L = ws_layout(d);
     float* T = (float*)(ws + L.T);
     dim3 grid(d.B - 1, d.batch);

@@ -71,7 +71,7 @@ def _load():
     lib_.dfs_status_string.argtypes = [I]
     lib_.dfs_status_string.restype = C.c_char_p
     lib_.dfs_validate_config.argtypes = [cfg]
-    lib_.dfs_conv.argtypes = [cfg, P, P, P, P, P]
+    lib_.dfs_conv.argtypes = [cfg, P, P, P, P, P, S, P]
     lib_.dfs_head_topk.argtypes = [cfg, P, P, P, P, P, P, P, S, P]
     lib_.dfs_topk_logits.argtypes = [cfg, P, P, P, P, P, S, P]
     lib_.dfs_select.argtypes = [cfg, P, P, P, P, P, P, P, P, P, S, P]
@@ -123,8 +123,9 @@ def validate_config(cfg: Config) -> int:
     return int(_lib.dfs_validate_config(C.byref(cfg)))
 
 
-def conv(cfg, h, wg_cm, y, y_f32=None, stream=None):
-    _check(_lib.dfs_conv(C.byref(cfg), _ptr(h), _ptr(wg_cm), _ptr(y), _ptr(y_f32), _stream(stream)), "dfs_conv")
+def conv(cfg, h, wg_cm, y, ws, y_f32=None, stream=None):
+    _check(_lib.dfs_conv(C.byref(cfg), _ptr(h), _ptr(wg_cm), _ptr(y), _ptr(y_f32), _ptr(ws), _nbytes(ws),
+                         _stream(stream)), "dfs_conv")
 
 
 def head_topk(cfg, y, W, cand_ids, cand_logp, lse, ws, logits_f32=None, stream=None):

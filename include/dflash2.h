@@ -110,11 +110,13 @@ int dfs_validate_config(const dfs_config* cfg);
  *                       the fp32 result
  *  y_f32  [rows, D]     fp32, optional (NULL): the fp32 result before
  *                       rounding, for parity checks
+ *  ws, ws_bytes         workspace (see conventions); the bf16 path keeps the
+ *                       partial tap logits of its split D reduction there
  * Positions before the start of a block count as zero; the tap softmax is
- * not renormalised there.  Needs no workspace.
+ * not renormalised there.
  */
 int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm,
-             void* y, float* y_f32, void* stream);
+             void* y, float* y_f32, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Steps 2-3: vocabulary head, log-softmax and per-slot top-K for every row.

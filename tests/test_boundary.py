@@ -96,13 +96,15 @@ def call(name, *args):
     return getattr(L, name)(*args)
 
 
-def conv_args(cfg, h=A, wg=A, y=A, yf=None):
-    return (C.byref(cfg), h, wg, y, yf, None)
+def conv_args(cfg, h=A, wg=A, y=A, yf=None, ws=A, nbytes=None):
+    if nbytes is None:
+        nbytes = dfs.workspace_size(cfg) if dfs.validate_config(cfg) == OK else 0
+    return (C.byref(cfg), h, wg, y, yf, ws, nbytes, None)
 
 
 def test_conv_validation():
     c = cfg_of(2)
-    assert L.dfs_conv(None, A, A, A, None, None) == NULL
+    assert L.dfs_conv(None, A, A, A, None, A, 1 << 20, None) == NULL
     assert call("dfs_conv", *conv_args(c, h=None)) == NULL
     assert call("dfs_conv", *conv_args(c, wg=None)) == NULL
     assert call("dfs_conv", *conv_args(c, y=None)) == NULL
@@ -110,6 +112,9 @@ def test_conv_validation():
     assert call("dfs_conv", *conv_args(c, yf=A + 4)) == MISAL
     assert call("dfs_conv", *conv_args(cfg_of(2, conv_kernel_size=3))) == UNSUP
     assert call("dfs_conv", *conv_args(cfg_of(2, hidden=100))) == SHAPE
+    assert call("dfs_conv", *conv_args(c, nbytes=dfs.workspace_size(c) - 1)) == WS
+    assert call("dfs_conv", *conv_args(c, ws=None)) == NULL
+    assert call("dfs_conv", *conv_args(c, ws=A + 16)) == MISAL
 
 
 def test_head_topk_validation():
@@ -178,5 +183,5 @@ def test_draft_block_validation():
 def test_binding_raises_typed_error():
     c = cfg_of(2, block_size=1)
     with pytest.raises(dfs.DFSError) as e:
-        dfs.conv(c, A, A, A, stream=0)
+        dfs.conv(c, A, A, A, None, stream=0)
     assert e.value.status == SHAPE and "DFS_ERR_SHAPE" in str(e.value)

@@ -80,7 +80,8 @@ def test_conv_parity(s):
     wg = to_dev(wg_channel_major(inp["wg"]))
     y = empty((s.rows, s.hidden), tdtype(s))
     yf = empty((s.rows, s.hidden), torch.float32)
-    dfs.conv(cfg, h, wg, y, yf)
+    ws = wsbuf(cfg)
+    dfs.conv(cfg, h, wg, y, ws, y_f32=yf)
     torch.cuda.synchronize()
     _, _, yhat = orc.conv(s, inp["h"], inp["wg"])
     yf_h = from_dev(yf)
@@ -92,7 +93,7 @@ def test_conv_parity(s):
         assert np.array_equal(y_h, yf_h)
     # the parity output does not change the product output
     y2 = empty((s.rows, s.hidden), tdtype(s))
-    dfs.conv(cfg, h, wg, y2, None)
+    dfs.conv(cfg, h, wg, y2, ws)
     torch.cuda.synchronize()
     assert np.array_equal(from_dev(y2), y_h)
 
