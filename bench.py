@@ -57,6 +57,21 @@ def head_flops(s) -> int:
     return 2 * s.rows * s.hidden * s.vocab
 
 
+def recorded_traffic(workload: int):
+    """HBM bytes per launch of the head + top-K stage from the committed
+    rocprofv3 counter record, or None if the record does not exist, is for
+    another workload, or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "head_traffic.json")
+    if workload != 2 or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -161,9 +176,12 @@ def main() -> int:
 
     hb = head_stage_bytes(s)
     achieved = hb / (us_head * 1e-6) / 1e9
+    traffic = recorded_traffic(args.workload)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "lm_head + top-K stage (head_pair_kernel + merge_kernel, one dfs_head_topk call)",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": round(traffic / (us_head * 1e-6) / 1e9, 1) if traffic else None,
+            "traffic_bytes_per_launch": traffic,
+            "kernel": "lm_head + top-K stage (head_pair_kernel + merge16_kernel, one dfs_head_topk call)",
             "bytes_per_launch": hb, "us_per_launch": round(us_head, 2)}
     if s.dtype != "bf16":
         roof["bound"] = "latency"
