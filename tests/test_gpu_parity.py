@@ -387,3 +387,47 @@ def test_draft_block_deterministic_and_stream():
         b = run_block(s, dev, stream=st)
     for x, y in zip(a, b):
         assert np.array_equal(x, y, equal_nan=True)
+
+
+def test_draft_block_long_block_planted():
+    """Long-block workload (batch 8, B 16) with transition plants: paths
+    against the oracle reference in tests/golden/plant_w4.json (written by
+    tests/golden/make_plant_w4.py from the oracle alone)."""
+    import json
+    import os
+
+    from plant import apply_plant
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "plant_w4.json")))
+    s = wl.shape_of(4)
+    inp, dev = cfg_inputs(4)
+    sites = [tuple(x) for x in g["sites"]]
+    Qp = apply_plant(s, inp["P"], inp["Q"], sites)
+    dev = dict(dev)
+    dev["Q"] = to_dev(Qp)
+    path, score, ids, lp = run_block(s, dev)
+    ref_ids = np.array(g["cand_ids"], np.int32)
+    bad_rows = [r for r in range(s.rows) if not np.array_equal(ids[r], ref_ids[r])]
+    if bad_rows:  # explain by oracle logits of those rows
+        for r in bad_rows:
+            b = r // s.block
+            rows = np.arange(b * s.block, (b + 1) * s.block)
+            sub = s.with_(batch=1)
+            _, _, yhat = orc.conv(sub, np.ascontiguousarray(inp["h"][rows]), inp["wg"])
+            y = orc.round_to(sub, yhat)
+            L = orc.head(sub, y, inp["W"], r0=r - b * s.block, nr=1, want_logits=True)["logits"][0]
+            gsort = np.sort(L[ids[r]])[::-1]
+            rsort = np.sort(L[ref_ids[r]])[::-1]
+            assert np.max(np.abs(gsort - rsort)) <= TOL * 3.0, f"row {r}"
+    near = 0
+    for b in range(s.batch):
+        same_cands = not any(b * s.block <= r < (b + 1) * s.block for r in bad_rows)
+        if g["margin"][b] > 1e-3 and same_cands:
+            assert path[b].tolist() == g["path"][b], f"block {b}"
+        else:
+            near += 1
+    assert near <= 2
+    assert rel_err(score, np.array(g["score"])) <= TOL
+    # the plants move the walk off the per-slot argmax where the oracle's does
+    dev_gpu = sum(path[b, t] != ids[b * s.block + t, 0] for b, t, *_ in sites)
+    assert dev_gpu == g["n_sites_deviating"]

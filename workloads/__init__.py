@@ -13,6 +13,7 @@ from .synth import (  # noqa: F401
     bf16_bits_to_f32,
     draw_normal,
     draw_anchor,
+    draw_plant_sites,
     make_inputs,
     make_inputs_for,
 )

@@ -124,6 +124,18 @@ def draw_anchor(seed: int, batch: int, vocab: int) -> np.ndarray:
     return g.integers(0, vocab, size=batch, dtype=np.int64).astype(np.int32)
 
 
+def draw_plant_sites(seed: int, batch: int, block: int, top_k: int, fraction: float = 0.10):
+    """Random plant sites for the long-block workload: round(fraction * batch
+    * (block - 1)) distinct (b, t) pairs with t in 1..block-1, each with a
+    candidate index k ~ U[1, top_k - 1] (never the slot's argmax)."""
+    g = _philox(seed, TENSOR_IDS["plant"], 0)
+    slots = batch * (block - 1)
+    n = int(round(fraction * slots))
+    pick = np.sort(g.choice(slots, size=n, replace=False))
+    ks = g.integers(1, top_k, size=n)
+    return [(int(i // (block - 1)), int(i % (block - 1)) + 1, int(k)) for i, k in zip(pick, ks)]
+
+
 def make_inputs_for(shape: Shape, seed: int, parts=("h", "wg", "W", "P", "Q", "anchor")) -> dict:
     """Draw the inputs of one workload.
 
