@@ -286,6 +286,215 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
     }
 }
 
+// Head for many rows (more than 8 per call, up to 256 per pass): a GEMM
+// logit[v][row] = <W[v], y[row]> on v_mfma_f32_32x32x16_bf16 with the same
+// fused per-chunk top-K and (max, sum of exp) as the streaming head.
+//  - One persistent workgroup per CU owns a contiguous vocabulary range and
+//    walks it in tiles of 256 rows of W against every hidden row.
+//  - Both operands arrive in 32-channel stages (W: 256 rows x 64 B, hidden
+//    rows: up to 256 x 64 B) by direct global->LDS loads into a four-stage
+//    LDS ring, three stages ahead of the MFMAs, without staging registers.
+//    Those loads are the only vector-memory operations of the main loop, so
+//    a fixed count of outstanding operations says when a stage has landed.
+//    They are issued from inline assembly: the compiler, unable to tell the
+//    ring slots apart, would otherwise wait for every load in flight before
+//    each LDS read.
+//  - LDS rows are 64 B (4 units of 16 B); unit u of row v is stored at unit
+//    u ^ ((v >> 2) & 3), so the 32-row operand reads of a wave hit distinct
+//    banks in every group of 16 lanes.
+//  - Wave w owns hidden rows 32w .. 32w+31 and all 256 vocabulary rows of
+//    the tile: 8 accumulator tiles of 32x32.  In that output layout a lane
+//    holds one hidden row (column l % 32) and 16 vocabulary entries per tile,
+//    so each lane keeps a sorted register list of its best keys and an online
+//    (max, sum of exp) for its row; the logits never leave registers.  At the
+//    end the two lanes of every row are merged into the chunk's partial.
+constexpr int kGemmTV = 256;
+constexpr int kGemmKC = 32;
+constexpr int kGemmRing = 4;
+constexpr int kGemmWBytes = kGemmTV * kGemmKC * 2;  // 16 KB of W per stage
+
+__device__ __forceinline__ int gemm_unit(int row, int u) { return row * 4 + (u ^ ((row >> 2) & 3)); }
+
+// 16-B global -> LDS copy per lane; lane L writes lds_base + 16 L.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(g)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+template <int NWB>
+__global__ __launch_bounds__(NWB * kWave) void head_gemm_kernel(
+    const uint16_t* __restrict__ y, int rows_total, int D, const uint16_t* __restrict__ W, int V, int nch, int K,
+    uint64_t* __restrict__ part_keys, float2* __restrict__ part_ms, float* __restrict__ logits) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int RP = 32 * NWB;
+    constexpr int KL = 16;
+    constexpr int YBYTES = RP * kGemmKC * 2;
+    constexpr int STAGE = kGemmWBytes + YBYTES;
+    constexpr int WI = kGemmWBytes / 1024 / NWB;  // W load instructions per wave per stage
+    constexpr int YI = YBYTES / 1024 / NWB;       // hidden-row load instructions per wave per stage
+    constexpr int OPS = WI + YI;                  // vector-memory operations per wave per stage
+    const int c = blockIdx.x;
+    const int row_base = blockIdx.y * RP;
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int j = lane & 31, half = lane >> 5;
+    const int rl = wave * 32 + j;
+    const int my_row = row_base + rl;
+    const bool row_ok = my_row < rows_total;
+    const int S = D / kGemmKC;
+
+    const int64_t T32 = ((int64_t)V + 31) / 32;
+    const int b_beg = (int)(T32 * c / nch), b_end = (int)(T32 * (c + 1) / nch);
+    const int v_beg = b_beg * 32, v_end = min(b_end * 32, V);
+    const int ntiles = (b_end - b_beg + 7) / 8;
+    const int total = ntiles * S;
+    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+
+    // Stage g (tile g / S, channels 32 (g % S) ..) into ring slot g % 4.  A
+    // 1 KB load instruction covers 16 rows x 64 B; lane L takes row L / 4,
+    // stored unit L % 4, i.e. logical unit (L % 4) ^ ((row >> 2) & 3).
+    auto issue_stage = [&](int g) {
+        const int tile = g / S, k0 = (g % S) * kGemmKC;
+        const uint32_t base = smem_base + (uint32_t)((g % kGemmRing) * STAGE);
+        const int v0 = v_beg + tile * kGemmTV;
+#pragma unroll
+        for (int i = 0; i < WI; ++i) {
+            const int n = wave + i * NWB;
+            const int vr = 16 * n + (lane >> 2);
+            const int u = (lane & 3) ^ ((vr >> 2) & 3);
+            const int v = min(v0 + vr, v_end - 1);  // past the range: re-read its last row (cache hit)
+            dma16(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < YI; ++i) {
+            const int n = wave + i * NWB;
+            const int r = 16 * n + (lane >> 2);
+            const int u = (lane & 3) ^ ((r >> 2) & 3);
+            const int row = min(row_base + r, rows_total - 1);
+            dma16(y + (size_t)row * D + k0 + 8 * u, base + kGemmWBytes + n * 1024);
+        }
+    };
+    // Wait until this wave's loads of stage g have landed, given that the
+    // stages up to g + 2 were issued after it (fewer near the end).
+    auto wait_stage = [&](int g) {
+        if (g + 2 < total)
+            __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | ((2 * OPS) & 0xF) | (((2 * OPS) >> 4) << 14));
+        else if (g + 1 < total)
+            __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (OPS & 0xF) | ((OPS >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4));
+    };
+
+    f32x16 acc[8];
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[vb][r] = 0.f;
+    uint64_t lst[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) lst[i] = 0ull;
+    MaxSum ms{-INFINITY, 0.f};
+
+    for (int g = 0; g < kGemmRing - 1 && g < total; ++g) issue_stage(g);
+    int tile = 0, st = 0;
+    for (int g = 0; g < total; ++g) {
+        wait_stage(g);
+        __syncthreads();  // stage g complete for every wave; slot (g - 1) % 4 free
+        if (g + kGemmRing - 1 < total) issue_stage(g + kGemmRing - 1);
+        const uint4* sw = (const uint4*)(smem + (size_t)(g % kGemmRing) * STAGE);
+        const uint4* sy = (const uint4*)(smem + (size_t)(g % kGemmRing) * STAGE + kGemmWBytes);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int u = 2 * ks + half;
+            const bf16x8 b = __builtin_bit_cast(bf16x8, sy[gemm_unit(rl, u)]);
+            // Rows past the range hold copies of its last row; their results
+            // are dropped below.
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit(vb * 32 + j, u)]);
+                acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[vb], 0, 0, 0);
+            }
+        }
+        if (st == S - 1) {
+            // Tile done.  Lane holds, for vocabulary block vb, logit[v][my_row]
+            // in acc[vb][r] with v = base + 32 vb + 8 (r / 4) + 4 half + r % 4.
+            const int vt = v_beg + tile * kGemmTV;
+            const int nvb = min(8, b_end - (b_beg + 8 * tile));
+            if (row_ok) {
+#pragma unroll
+                for (int vb = 0; vb < 8; ++vb) {
+                    if (vb < nvb) {
+                        float mnew = ms.m;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int v = vt + 32 * vb + 8 * (r >> 2) + 4 * half + (r & 3);
+                            if (v < v_end) mnew = fmaxf(mnew, acc[vb][r]);
+                        }
+                        float sacc = (ms.m == -INFINITY) ? 0.f : ms.s * __expf(ms.m - mnew);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int v = vt + 32 * vb + 8 * (r >> 2) + 4 * half + (r & 3);
+                            if (v < v_end) {
+                                const float x = acc[vb][r];
+                                sacc += __expf(x - mnew);
+                                const uint64_t key = make_key(x, (uint32_t)v);
+                                if (key > lst[KL - 1]) list_insert<KL>(lst, key);
+                                if (logits) logits[(size_t)my_row * V + v] = x;
+                            }
+                        }
+                        ms = MaxSum{mnew, sacc};
+                    }
+                }
+            }
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[vb][r] = 0.f;
+            ++tile;
+            st = 0;
+        } else {
+            ++st;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every read of the ring done before it holds the lists
+
+    // The two lanes of each row -> the chunk's partial.
+    uint64_t* Lm = (uint64_t*)smem;                                // [RP][2][K]
+    float2* Mm = (float2*)(smem + (size_t)RP * 2 * K * 8);       // [RP][2]
+    if (row_ok) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+            if (i < K) Lm[((size_t)rl * 2 + half) * K + i] = lst[i];
+        Mm[rl * 2 + half] = make_float2(ms.m, ms.s);
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < RP; r += NWB * kWave) {
+        const int row = row_base + r;
+        if (row >= rows_total) continue;
+        const uint64_t* a = Lm + (size_t)r * 2 * K;
+        const uint64_t* b = a + K;
+        int ia = 0, ib = 0;
+        uint64_t* out = part_keys + (size_t)row * K * nch + c;
+        for (int i = 0; i < K; ++i) {
+            const uint64_t ka = a[ia], kb = b[ib];
+            if (ka >= kb) {
+                out[(size_t)i * nch] = ka;
+                ++ia;
+            } else {
+                out[(size_t)i * nch] = kb;
+                ++ib;
+            }
+        }
+        const float2 m0 = Mm[r * 2], m1 = Mm[r * 2 + 1];
+        const MaxSum z = ms_combine(MaxSum{m0.x, m0.y}, MaxSum{m1.x, m1.y});
+        part_ms[(size_t)row * nch + c] = make_float2(z.m, z.s);
+    }
+}
+
 // fp32 correctness path: plain dot products, logits written out.
 __global__ __launch_bounds__(256) void head_f32_kernel(const float* __restrict__ y, const float* __restrict__ W,
                                                        float* __restrict__ logits, int rows, int D, int V) {
@@ -548,10 +757,32 @@ hipError_t launch_head_pair_t(const Dims& d, int K, const void* y, const void* W
     return hipGetLastError();
 }
 
-// Weight stream of the head for rows <= 8 per pass.  The whole-line kernel
-// needs D % 64 == 0 and a k-step count divisible by its prefetch depth.
+template <int NWB>
+hipError_t launch_head_gemm_t(const Dims& d, int K, const void* y, const void* W, int nch, uint64_t* keys,
+                              float2* ms, float* logits, hipStream_t s) {
+    constexpr int RP = 32 * NWB;
+    constexpr size_t ring = (size_t)kGemmRing * (kGemmWBytes + RP * kGemmKC * 2);
+    static_assert(ring <= 160 * 1024, "the stage ring must fit in LDS");
+    const size_t lds = std::max(ring, (size_t)RP * 2 * K * 8 + (size_t)RP * 2 * 8);
+    auto fn = head_gemm_kernel<NWB>;
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    dim3 grid(nch, (d.rows() + RP - 1) / RP);
+    fn<<<grid, NWB * kWave, lds, s>>>((const uint16_t*)y, d.rows(), d.D, (const uint16_t*)W, d.V, nch, K, keys, ms,
+                                      logits);
+    return hipGetLastError();
+}
+
+// Head dispatch.  Rows <= 8: the weight-stream kernel (whole-line variant
+// when D % 64 == 0).  More rows: the GEMM head.
 hipError_t launch_head_stream(const Dims& d, int K, const void* y, const void* W, int nch, uint64_t* keys,
                               float2* ms, float* logits, hipStream_t s) {
+    if (d.rows() > 8 && d.D % kGemmKC == 0) {
+        // many rows: one pass of the GEMM head per 256 rows instead of one
+        // weight stream per 8 rows
+        return d.rows() <= 128 ? launch_head_gemm_t<4>(d, K, y, W, nch, keys, ms, logits, s)
+                               : launch_head_gemm_t<8>(d, K, y, W, nch, keys, ms, logits, s);
+    }
     if (d.D % 64 == 0) {
         const int S = d.D / 64;
         if (S % 8 == 0) return launch_head_pair_t<8, 8>(d, K, y, W, nch, keys, ms, logits, s);
