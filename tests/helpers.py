@@ -64,3 +64,22 @@ def ids_match_or_explained(gpu_ids, ref_ids, ref_logits_row_fn, tol_abs):
         if np.max(np.abs(g - r)) > tol_abs:
             bad.append(i)
     return bad
+
+
+def topk_of(logits, K):
+    """Direct check of a top-K result against the logits it was taken from:
+    the K largest entries of each row (larger first, equal values by smaller
+    id, -0 equal to +0) and the row's log-sum-exp in fp64.  A property of the
+    returned logits, not a second implementation of the method."""
+    L = np.asarray(logits, np.float32)
+    rows, V = L.shape
+    kth = np.partition(L, V - K, axis=1)[:, V - K]
+    ids = np.empty((rows, K), np.int32)
+    for i in range(rows):
+        cand = np.nonzero(L[i] >= kth[i])[0]
+        order = np.lexsort((cand, -L[i, cand].astype(np.float64)))
+        ids[i] = cand[order[:K]]
+    Ld = L.astype(np.float64)
+    m = Ld.max(axis=1)
+    lse = m + np.log(np.exp(Ld - m[:, None]).sum(axis=1))
+    return ids, lse

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from helpers import as_f64, empty, from_dev, ids_match_or_explained, rel_err, to_dev, wg_channel_major
+from helpers import as_f64, empty, from_dev, ids_match_or_explained, rel_err, to_dev, topk_of, wg_channel_major
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -126,19 +126,29 @@ def run_head(s, y_np, W_np, W_dev=None, with_logits=True):
     return (from_dev(ids), from_dev(lp), from_dev(lse), from_dev(logits) if with_logits else None)
 
 
-def check_head_fed(s, y_np, W_np, W_dev=None):
+def check_head_fed(s, y_np, W_np, W_dev=None, rows=None):
     ids, lp, lse, logits = run_head(s, y_np, W_np, W_dev)
-    # (i) ids are exactly the top-K of the GPU's own fp32 logits
-    rid, rlp, rlse = orc.topk(logits.astype(np.float64), s.top_k)
+    # (i) ids are exactly the top-K of the GPU's own fp32 logits, by a direct sort
+    rid, rlse = topk_of(logits, s.top_k)
     assert np.array_equal(ids, rid)
     assert rel_err(lse, rlse) <= 1e-5
     # scores are logit - lse in fp32
     want = (np.take_along_axis(logits, ids, 1) - lse[:, None]).astype(np.float32)
     assert np.array_equal(lp, want)
-    # (iv) logits against the oracle head fed the same y
-    ref = orc.head(s, y_np, W_np, want_logits=True)
-    assert rel_err(logits, ref["logits"]) <= TOL
-    assert rel_err(lse, ref["lse"]) <= TOL
+    # (ii) logits, lse and ids against the oracle head fed the same y: every
+    # row, or the sampled rows one by one
+    if rows is None:
+        ref = orc.head(s, y_np, W_np, want_logits=True)
+        assert rel_err(logits, ref["logits"]) <= TOL
+        assert rel_err(lse, ref["lse"]) <= TOL
+        assert not ids_match_or_explained(ids, ref["ids"], lambda i: ref["logits"][i], tol_abs=TOL * 3.0)
+    else:
+        for r in rows:
+            ref = orc.head(s, y_np, W_np, r0=r, nr=1, want_logits=True)
+            assert rel_err(logits[r], ref["logits"][0]) <= TOL
+            assert rel_err(lse[r], ref["lse"][0]) <= TOL
+            assert not ids_match_or_explained(ids[r:r + 1], ref["ids"], lambda i: ref["logits"][0],
+                                              tol_abs=TOL * 3.0)
     # the timed mode (no logits written) returns the same candidates
     ids2, lp2, lse2, _ = run_head(s, y_np, W_np, W_dev, with_logits=False)
     assert np.array_equal(ids2, ids) and np.array_equal(lp2, lp) and np.array_equal(lse2, lse)
@@ -431,3 +441,12 @@ def test_draft_block_long_block_planted():
     # the plants move the walk off the per-slot argmax where the oracle's does
     dev_gpu = sum(path[b, t] != ids[b * s.block + t, 0] for b, t, *_ in sites)
     assert dev_gpu == g["n_sites_deviating"]
+
+
+def test_head_topk_fed_many_rows():
+    """GEMM head at the batch-32 page shape (256 rows): ids exactly the top-K
+    of the GPU's own logits for every row; logits, lse and ids against the
+    oracle head on sampled rows."""
+    s = wl.shape_of(3)
+    inp, dev = cfg_inputs(3)
+    check_head_fed(s, inp["h"], inp["W"], W_dev=dev["W"], rows=(0, 77, 255))
