@@ -13,6 +13,7 @@ constexpr int kMaxRows = 65536;
 constexpr int kMaxHidden = 65536;
 constexpr int kMaxHiddenBf16Head = 8192;  // hidden rows stay resident in LDS
 constexpr int kMaxTapsF32 = 4096;         // fp32 conv keeps z and w in LDS (32 KB)
+constexpr int kMaxVocab = 1 << 21;        // logits ranked in at most 256 slices of 8192
 
 bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
 
@@ -27,7 +28,8 @@ int check_cfg(const dfs_config* c) {
     if (c->conv_kernel_size != 1 && c->conv_kernel_size != 2 && c->conv_kernel_size != 4) return DFS_ERR_UNSUPPORTED;
     if (c->top_k < 1) return DFS_ERR_SHAPE;
     if (c->top_k > 64) return DFS_ERR_UNSUPPORTED;
-    if (c->vocab < c->top_k || c->vocab > INT32_MAX - 64) return DFS_ERR_SHAPE;
+    if (c->vocab < c->top_k) return DFS_ERR_SHAPE;
+    if (c->vocab > kMaxVocab) return DFS_ERR_UNSUPPORTED;
     if (c->rank < 8 || c->rank % 8 != 0 || c->rank > 4096) return DFS_ERR_SHAPE;
     if (c->dtype == DFS_BF16 && c->hidden > kMaxHiddenBf16Head) return DFS_ERR_UNSUPPORTED;
     if (c->dtype == DFS_F32 && (int64_t)(c->hidden / c->conv_group_size) * c->conv_kernel_size > kMaxTapsF32)

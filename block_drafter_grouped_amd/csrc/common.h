@@ -99,6 +99,15 @@ __device__ __forceinline__ float wave_max_f32(float x) {
     return fmaxf(fmaxf(readlane_f32(x, 0), readlane_f32(x, 16)), fmaxf(readlane_f32(x, 32), readlane_f32(x, 48)));
 }
 
+// Sum in a fixed order (the same result on every run).
+__device__ __forceinline__ float wave_sum_f32(float x) {
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppHalfMirror>(x);
+    x += dpp_f32<kDppMirror>(x);
+    return (readlane_f32(x, 0) + readlane_f32(x, 16)) + (readlane_f32(x, 32) + readlane_f32(x, 48));
+}
+
 // Online (max, sum of exp) pair: value set {x} is represented by
 // m = max x and s = sum exp(x - m).  m = -inf, s = 0 is the empty set.
 struct MaxSum {

@@ -34,16 +34,17 @@ size_t conv_ws_bytes(const Dims& d);
 hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32, char* ws,
                        hipStream_t s);
 
-// Head + top-K.  Uses ws.keys / ws.ms (and ws.logits for fp32 if logits_f32
-// is NULL).
+// Head + top-K.  Uses ws.keys / ws.ms, and ws.logits when the logits are
+// ranked after the head (fp32, K > 16, more than 8 rows) and logits_f32 is
+// NULL.
 hipError_t launch_head_topk(const Dims& d, const void* y, const void* W, int32_t* cand_ids,
                             float* cand_logp, float* lse, float* logits_f32, char* ws,
                             hipStream_t s);
 
-// The head's per-chunk partials only (no merge); used by the whole-block
-// path, whose final kernel merges them.
+// The head's per-chunk partials only (no merge); *nparts receives the number
+// of chunks the merge reads.
 hipError_t launch_head_partials(const Dims& d, const void* y, const void* W, float* logits_f32, char* ws,
-                                hipStream_t s);
+                                int* nparts, hipStream_t s);
 
 hipError_t launch_topk_logits(const Dims& d, const float* logits, int32_t* cand_ids, float* cand_logp,
                               float* lse, char* ws, hipStream_t s);

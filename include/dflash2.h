@@ -75,7 +75,7 @@ typedef struct {
     int32_t batch;            /* independent blocks, >= 1                         */
     int32_t block_size;       /* B = 1 + draft slots, 2..64                       */
     int32_t hidden;           /* D, a multiple of 32 and of conv_group_size       */
-    int32_t vocab;            /* V, top_k <= V < 2^31 - 1                          */
+    int32_t vocab;            /* V, top_k <= V <= 2^21 (2 097 152)                 */
     int32_t top_k;            /* K = selector_top_k, 1..64                         */
     int32_t rank;             /* r = selector_rank, a multiple of 8, 8..4096       */
     int32_t conv_group_size;  /* channels sharing one generated kernel (16)        */

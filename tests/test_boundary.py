@@ -60,7 +60,7 @@ def test_workload_configs_are_valid(cfg_id):
     ("hidden", 48, SHAPE), ("hidden", 0, SHAPE), ("hidden", 16384, UNSUP),
     ("conv_group_size", 0, SHAPE), ("conv_group_size", 48, SHAPE),
     ("conv_kernel_size", 0, SHAPE), ("conv_kernel_size", 3, UNSUP), ("conv_kernel_size", 8, UNSUP),
-    ("top_k", 0, SHAPE), ("top_k", 65, UNSUP), ("vocab", 15, SHAPE),
+    ("top_k", 0, SHAPE), ("top_k", 65, UNSUP), ("vocab", 15, SHAPE), ("vocab", (1 << 21) + 1, UNSUP),
     ("rank", 0, SHAPE), ("rank", 12, SHAPE), ("rank", 8192, SHAPE), ("dtype", 7, UNSUP),
 ])
 def test_config_rules(field, value, status):
@@ -76,6 +76,7 @@ def test_config_rule_allowed_edges():
     assert dfs.validate_config(cfg_of(2, conv_kernel_size=1)) == OK
     assert dfs.validate_config(cfg_of(2, conv_kernel_size=4)) == OK
     assert dfs.validate_config(cfg_of(2, vocab=16)) == OK
+    assert dfs.validate_config(cfg_of(2, vocab=1 << 21)) == OK
     assert dfs.validate_config(cfg_of(0, hidden=16384, conv_group_size=16)) == OK  # fp32 has no LDS-resident head
     assert dfs.validate_config(cfg_of(2, batch=8192, block_size=8)) == OK
     assert dfs.validate_config(cfg_of(2, batch=8193, block_size=8)) == SHAPE

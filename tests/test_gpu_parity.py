@@ -110,6 +110,11 @@ HEAD_SHAPES = [
     S(block=8, hidden=256, vocab=3000, top_k=64),
     S(batch=5, block=1 + 1, hidden=64, vocab=16, top_k=16),
     S(block=6, hidden=96, vocab=3001, top_k=7, dtype="f32"),
+    # more than 8 rows: the GEMM head and the slice top-K of its logits
+    S(batch=3, block=3, hidden=32, vocab=100, top_k=16),
+    S(batch=4, block=8, hidden=96, vocab=3001, top_k=16),
+    S(batch=20, block=8, hidden=128, vocab=70000, top_k=64),
+    S(batch=40, block=8, hidden=64, vocab=5000, top_k=5),
 ]
 
 
@@ -184,10 +189,18 @@ def crafted_logits(rows, V, seed):
     if rows > 4:
         step = max(1, V // 300)
         L[4, ::step] = 7.0  # many exact ties across chunk boundaries
+    if rows > 5:
+        # Large values at the ids v with v % 1024 < 224.  With slices that
+        # start at multiples of 1024 they fall in fewer lane groups than K, so
+        # more keys than the gather buffer holds pass the group-maximum
+        # threshold and the exact bisection decides.
+        big = (np.arange(V) % 1024) < 224
+        L[5:, big] = 1000.0 + np.round(rng.standard_normal((rows - 5, int(big.sum()))) * 64) / 8
     return L
 
 
-@pytest.mark.parametrize("rows,V,K", [(6, 1537, 16), (6, 1537, 64), (5, 248320, 16), (7, 100, 1), (6, 64, 64)])
+@pytest.mark.parametrize("rows,V,K", [(6, 1537, 16), (6, 1537, 64), (5, 248320, 16), (7, 100, 1), (6, 64, 64),
+                                      (64, 32 * 7168, 16), (64, 32 * 7168, 64)])
 def test_topk_logits_crafted(rows, V, K):
     s = wl.Shape(batch=1, block=rows, hidden=64, vocab=V, top_k=K, rank=16, group=16, ksize=2, dtype="f32")
     cfg = dfs.Config.of(s)
