@@ -59,17 +59,26 @@ def head_flops(s) -> int:
 
 def recorded_traffic(workload: int):
     """HBM bytes per launch of the head + top-K stage from the committed
-    rocprofv3 counter record, or None if the record does not exist, is for
-    another workload, or the kernel sources changed since it was taken."""
+    rocprofv3 counter records, or None if there is no record for this
+    workload or the kernel sources changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "head_traffic.json")
-    if workload != 2 or not os.path.exists(path):
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in rec["sources"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+    for rec in json.load(open(path))["records"]:
+        if rec["workload"] != workload:
+            continue
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+    return None
+
+
+def uses_gemm_head(s) -> bool:
+    """More than 8 rows in bf16: the library's GEMM head writes the logits
+    and the slice top-K ranks them."""
+    return s.dtype == "bf16" and s.rows > 8
 
 
 def cpu_model() -> str:
@@ -175,14 +184,25 @@ def main() -> int:
     us_sel = timed(lambda: dfs.select(cfg, anchor, ids, lp, P, Q, path, score, ws, stream=stream))
 
     hb = head_stage_bytes(s)
-    achieved = hb / (us_head * 1e-6) / 1e9
     traffic = recorded_traffic(args.workload)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": round(traffic / (us_head * 1e-6) / 1e9, 1) if traffic else None,
-            "traffic_bytes_per_launch": traffic,
-            "kernel": "lm_head + top-K stage (head_pair_kernel + merge16_kernel, one dfs_head_topk call)",
-            "bytes_per_launch": hb, "us_per_launch": round(us_head, 2)}
+    traffic_gbs = round(traffic / (us_head * 1e-6) / 1e9, 1) if traffic else None
+    if uses_gemm_head(s):
+        # The contraction is large enough to be bound by the matrix cores.
+        fl = head_flops(s)
+        achieved = fl / (us_head * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic_gbs,
+                "traffic_unit": "GB/s", "traffic_bytes_per_launch": traffic,
+                "kernel": "lm_head + top-K stage (head_gemm_kernel + slice_topk_kernel + merge16_kernel, "
+                          "one dfs_head_topk call)",
+                "flops_per_launch": fl, "bytes_per_launch": hb, "us_per_launch": round(us_head, 2)}
+    else:
+        achieved = hb / (us_head * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_gbs,
+                "traffic_bytes_per_launch": traffic,
+                "kernel": "lm_head + top-K stage (head_pair_kernel + merge16_kernel, one dfs_head_topk call)",
+                "bytes_per_launch": hb, "us_per_launch": round(us_head, 2)}
     if s.dtype != "bf16":
         roof["bound"] = "latency"
 

@@ -1,0 +1,262 @@
+// Step 2 of the draft-block path for more than 8 rows (vLLM release-note
+// article on DFlash2, section "two additions": the target's lm_head and
+// log-softmax over the block's rows): the logits of every row as one GEMM,
+// and the fp32 head.  Both write fp32 logits; slice_topk.hip ranks them.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dfs {
+
+namespace {
+
+// Head for many rows (more than 8 per call, up to 256 per pass): a GEMM
+// logit[v][row] = <W[v], y[row]> on v_mfma_f32_32x32x16_bf16 that writes
+// the fp32 logits; the slice top-K kernel below ranks them.
+//  - One persistent workgroup per CU owns a contiguous vocabulary range and
+//    walks it in tiles of 256 rows of W against every hidden row, in stages
+//    of KC channels (64 when D % 64 == 0, else 32).
+//  - Producer and consumer waves.  NWB consumer waves each own 32 hidden
+//    rows and all 256 vocabulary rows of the tile (8 accumulator tiles of
+//    32x32); they only read LDS, issue MFMAs and store logits.  Four
+//    producer waves move the operands by direct global->LDS loads, two for W
+//    (a ring of RW stages) and two for the hidden rows (RY stages; L2
+//    resident, so a shallower ring).  A wave's count of outstanding memory
+//    operations drains in order for its own loads, so each producer waits on
+//    exactly its own stage; one barrier per stage then publishes it.  The
+//    consumers' logit stores never sit in front of a load in any wave's
+//    count, so they drain while the next tile computes.
+//  - The loads are issued from inline assembly: the compiler, unable to tell
+//    the ring slots apart, would otherwise wait for every load in flight
+//    before each LDS read.
+//  - An LDS row holds KC / 8 units of 16 B; unit u of row v is stored at
+//    unit u ^ f(v) with f(v) = (v >> 2) & 3 (4 units) or (v >> 1) & 7 (8
+//    units), so the 32-row operand reads of a wave hit distinct banks in
+//    every group of 16 lanes.
+//  - In the 32x32 output layout a lane holds one hidden row and, per tile,
+//    4 runs of 4 consecutive vocabulary entries, stored as 16-B writes.
+// Ranking inside this kernel (a sorted per-lane list) was tried first: the
+// lists of the 64 lanes of a wave take their insertions at different values,
+// so the wave ran nearly every insertion and the epilogue cost about a
+// quarter of the kernel.  Writing the logits costs a tenth of the weight
+// stream and the ranking then runs at the speed of reading them.
+constexpr int kGemmTV = 256;
+
+template <int KC>
+__device__ __forceinline__ int gemm_swz(int row) {
+    return KC == 32 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+}
+template <int KC>
+__device__ __forceinline__ int gemm_unit(int row, int u) {
+    return row * (KC / 8) + (u ^ gemm_swz<KC>(row));
+}
+
+// 16-B global -> LDS copy per lane; lane L writes lds_base + 16 L.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(g)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+constexpr int kGemmProducers = 4;  // two W loaders, two hidden-row loaders
+
+// s_waitcnt with at most n vector-memory operations outstanding (n a
+// multiple of 4 up to 48: the counts the producers use).
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+#define DFS_WAIT_VM(k)                                                                          \
+    case k:                                                                                     \
+        __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | ((k) & 0xF) | (((k) >> 4) << 14)); \
+        break;
+        DFS_WAIT_VM(4) DFS_WAIT_VM(8) DFS_WAIT_VM(12) DFS_WAIT_VM(16) DFS_WAIT_VM(20) DFS_WAIT_VM(24)
+        DFS_WAIT_VM(28) DFS_WAIT_VM(32) DFS_WAIT_VM(36) DFS_WAIT_VM(40) DFS_WAIT_VM(44) DFS_WAIT_VM(48)
+#undef DFS_WAIT_VM
+        default:
+            __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4));
+            break;
+    }
+}
+
+template <int NWB, int KC, int RW, int RY>
+__global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kernel(
+    const uint16_t* __restrict__ y, int rows_total, int D, const uint16_t* __restrict__ W, int V, int nch,
+    float* __restrict__ logits) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int RP = 32 * NWB;
+    constexpr int UPR = KC / 8;                 // 16-B units per LDS row
+    constexpr int RPI = kWave / UPR;            // rows per 1-KB load instruction
+    constexpr int WBYTES = kGemmTV * KC * 2;    // one W stage
+    constexpr int YBYTES = RP * KC * 2;         // one hidden-row stage
+    constexpr int WI = WBYTES / 1024 / 2;       // load instructions per W producer per stage
+    constexpr int YI = YBYTES / 1024 / 2;       // per hidden-row producer per stage
+    static_assert(WI * 2048 == WBYTES && YI * 2048 == YBYTES, "whole load instructions per producer");
+    static_assert((RW - 2) * WI <= 48 && (RW - 2) * WI % 4 == 0 && (RY - 2) * YI <= 48 && (RY - 2) * YI % 4 == 0,
+                  "wait counts");
+    const int c = blockIdx.x;
+    const int row_base = blockIdx.y * RP;
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int S = D / KC;
+    const int64_t T32 = ((int64_t)V + 31) / 32;
+    const int b_beg = (int)(T32 * c / nch), b_end = (int)(T32 * (c + 1) / nch);
+    const int v_beg = b_beg * 32, v_end = min(b_end * 32, V);
+    const int ntiles = (b_end - b_beg + 7) / 8;
+    const int total = ntiles * S;
+    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+    const uint32_t ybase = smem_base + RW * WBYTES;
+
+    if (wave >= NWB) {
+        // Producers.  Stage g (tile g / S, channel block g % S) goes to slot
+        // g % RW (W) or g % RY (hidden rows).  A 1-KB load instruction covers
+        // RPI rows x 2 KC bytes; lane L takes row L / UPR, stored unit
+        // L % UPR, i.e. logical unit (L % UPR) ^ f(row).
+        const bool wl = wave < NWB + 2;
+        const int pw = wl ? wave - NWB : wave - NWB - 2;
+        auto issue_w = [&](int g) {
+            const int k0 = (g % S) * KC, v0 = v_beg + (g / S) * kGemmTV;
+            const uint32_t base = smem_base + (uint32_t)((g % RW) * WBYTES);
+#pragma unroll
+            for (int i = 0; i < WI; ++i) {
+                const int n = pw + 2 * i;
+                const int vr = RPI * n + lane / UPR;
+                const int u = (lane % UPR) ^ gemm_swz<KC>(vr);
+                const int v = min(v0 + vr, v_end - 1);  // past the range: re-read its last row (cache hit)
+                dma16(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
+            }
+        };
+        auto issue_y = [&](int g) {
+            const int k0 = (g % S) * KC;
+            const uint32_t base = ybase + (uint32_t)((g % RY) * YBYTES);
+#pragma unroll
+            for (int i = 0; i < YI; ++i) {
+                const int n = pw + 2 * i;
+                const int r = RPI * n + lane / UPR;
+                const int u = (lane % UPR) ^ gemm_swz<KC>(r);
+                const int row = min(row_base + r, rows_total - 1);
+                dma16(y + (size_t)row * D + k0 + 8 * u, base + n * 1024);
+            }
+        };
+        const int R = wl ? RW : RY, per = wl ? WI : YI;
+        for (int g = 0; g < R - 1 && g < total; ++g) wl ? issue_w(g) : issue_y(g);
+        for (int g = 0; g < total; ++g) {
+            // stage g landed: at most the later stages' loads outstanding
+            wait_vm(min(R - 2, total - 1 - g) * per);
+            __syncthreads();  // publish stage g; the slot read in stage g - 1 is free
+            if (g + R - 1 < total) wl ? issue_w(g + R - 1) : issue_y(g + R - 1);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+
+    // Consumers.
+    const int j = lane & 31, half = lane >> 5;
+    const int rl = wave * 32 + j;
+    const int my_row = row_base + rl;
+    const bool row_ok = my_row < rows_total;
+    const bool vec4 = (V & 3) == 0;  // rows of the logits are 16-B aligned
+    f32x16 acc[8];
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[vb][r] = 0.f;
+    int tile = 0, st = 0;
+    for (int g = 0; g < total; ++g) {
+        __syncthreads();  // stage g published
+        const uint4* sw = (const uint4*)(smem + (size_t)(g % RW) * WBYTES);
+        const uint4* sy = (const uint4*)(smem + (size_t)RW * WBYTES + (size_t)(g % RY) * YBYTES);
+#pragma unroll
+        for (int ks = 0; ks < KC / 16; ++ks) {
+            const int u = 2 * ks + half;
+            const bf16x8 b = __builtin_bit_cast(bf16x8, sy[gemm_unit<KC>(rl, u)]);
+            // Rows past the range hold copies of its last row; their results
+            // are dropped below.
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit<KC>(vb * 32 + j, u)]);
+                acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[vb], 0, 0, 0);
+            }
+        }
+        if (st == S - 1) {
+            // Tile done.  Lane holds, for vocabulary block vb, logit[v][my_row]
+            // in acc[vb][r] with v = base + 32 vb + 8 (r / 4) + 4 half + r % 4.
+            const int vt = v_beg + tile * kGemmTV;
+            if (row_ok) {
+                float* out = logits + (size_t)my_row * V;
+#pragma unroll
+                for (int vb = 0; vb < 8; ++vb) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int v = vt + 32 * vb + 8 * q + 4 * half;
+                        if (vec4 && v + 3 < v_end) {
+                            *(f32x4*)(out + v) = f32x4{acc[vb][4 * q], acc[vb][4 * q + 1], acc[vb][4 * q + 2],
+                                                       acc[vb][4 * q + 3]};
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (v + e < v_end) out[v + e] = acc[vb][4 * q + e];
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[vb][r] = 0.f;
+            ++tile;
+            st = 0;
+        } else {
+            ++st;
+        }
+    }
+}
+
+// fp32 correctness path: plain dot products, logits written out.
+__global__ __launch_bounds__(256) void head_f32_kernel(const float* __restrict__ y, const float* __restrict__ W,
+                                                       float* __restrict__ logits, int rows, int D, int V) {
+    const int v = blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= V) return;
+    for (int row = 0; row < rows; ++row) {
+        float acc = 0.f;
+        for (int c = 0; c < D; ++c) acc += y[(size_t)row * D + c] * W[(size_t)v * D + c];
+        logits[(size_t)row * V + v] = acc;
+    }
+}
+
+}  // namespace
+
+template <int NWB, int KC, int RW, int RY>
+hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int nch, float* logits, hipStream_t s) {
+    constexpr int RP = 32 * NWB;
+    constexpr size_t lds = ((size_t)RW * kGemmTV + (size_t)RY * RP) * KC * 2;
+    static_assert(lds <= 160 * 1024, "the stage rings must fit in LDS");
+    auto fn = head_gemm_kernel<NWB, KC, RW, RY>;
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    dim3 grid(nch, (d.rows() + RP - 1) / RP);
+    fn<<<grid, (NWB + kGemmProducers) * kWave, lds, s>>>((const uint16_t*)y, d.rows(), d.D, (const uint16_t*)W, d.V,
+                                                         nch, logits);
+    return hipGetLastError();
+}
+
+// More than 8 rows: one pass of the GEMM head per 256 rows instead of one
+// weight stream per 8 rows.
+bool use_gemm_head(const Dims& d) { return d.bf16 && d.rows() > kRowsPass; }
+
+hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {
+    const int nch = head_chunks(d);
+    if (d.D % 64 == 0)
+        return d.rows() <= 128 ? launch_head_gemm_t<4, 64, 3, 2>(d, y, W, nch, logits, s)
+                               : launch_head_gemm_t<8, 64, 3, 2>(d, y, W, nch, logits, s);
+    return d.rows() <= 128 ? launch_head_gemm_t<4, 32, 6, 4>(d, y, W, nch, logits, s)
+                           : launch_head_gemm_t<8, 32, 6, 4>(d, y, W, nch, logits, s);
+}
+
+hipError_t launch_head_f32(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {
+    head_f32_kernel<<<(d.V + 255) / 256, 256, 0, s>>>((const float*)y, (const float*)W, logits, d.rows(), d.D, d.V);
+    return hipGetLastError();
+}
+
+}  // namespace dfs

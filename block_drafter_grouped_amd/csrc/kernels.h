@@ -17,6 +17,8 @@ struct Dims {
     int taps() const { return groups() * ks; }  // columns of the generator
 };
 
+constexpr int kRowsPass = 8;  // rows one pass of the streaming head serves
+
 // Number of vocabulary chunks whose per-chunk top-K / (max, sum) partials the
 // head writes.  A function of the shape only, so workspace sizes need no
 // device query.
@@ -45,6 +47,18 @@ hipError_t launch_head_topk(const Dims& d, const void* y, const void* W, int32_t
 // of chunks the merge reads.
 hipError_t launch_head_partials(const Dims& d, const void* y, const void* W, float* logits_f32, char* ws,
                                 int* nparts, hipStream_t s);
+
+// Heads that write fp32 logits [rows][V]: the GEMM head (bf16, more than
+// kRowsPass rows) and the fp32 head.
+bool use_gemm_head(const Dims& d);
+hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s);
+hipError_t launch_head_f32(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s);
+
+// Per-slice top-K keys and (max, sum of exp) of written logits, in the
+// partial layout the merge reads ([row][k][slice], stride nsl).
+int logits_slices(const Dims& d);
+hipError_t launch_logits_partials(const Dims& d, const float* logits, int nsl, uint64_t* keys, float2* ms,
+                                  hipStream_t s);
 
 hipError_t launch_topk_logits(const Dims& d, const float* logits, int32_t* cand_ids, float* cand_logp,
                               float* lse, char* ws, hipStream_t s);
