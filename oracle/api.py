@@ -29,9 +29,9 @@ def load():
         lib.orc_round.restype = None
         lib.orc_head.argtypes = [C.POINTER(_Shape), P, P, C.c_int, C.c_int, P, P, P, P]
         lib.orc_topk.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P]
-        lib.orc_transitions.argtypes = [C.POINTER(_Shape), C.c_int32, P, P, P, P]
+        lib.orc_transitions.argtypes = [C.POINTER(_Shape), C.c_int32, P, P, P, P, P]
         lib.orc_viterbi.argtypes = [C.c_int, C.c_int, P, P, P, P, P]
-        lib.orc_draft_block.argtypes = [C.POINTER(_Shape)] + [P] * 13
+        lib.orc_draft_block.argtypes = [C.POINTER(_Shape)] + [P] * 14
         lib.orc_threads.argtypes = []
         _LIB = lib
     return _LIB
@@ -104,13 +104,24 @@ def topk(logits: np.ndarray, K: int):
     return ids, logp, lse
 
 
-def transitions(s, anchor: int, ids_block: np.ndarray, P, Q) -> np.ndarray:
-    """T [B-1, K, K] for one block; ids_block [B, K] (row 0 ignored)."""
+def _gate(gate, rows, s):
+    if gate is None:
+        return None
+    g = np.ascontiguousarray(gate, dtype=np.float64)
+    if g.shape != (rows, s.rank):
+        raise ValueError(f"gate must be [{rows}, {s.rank}]")
+    return g
+
+
+def transitions(s, anchor: int, ids_block: np.ndarray, P, Q, gate=None) -> np.ndarray:
+    """T [B-1, K, K] for one block; ids_block [B, K] (row 0 ignored); gate
+    [B, r] or None (all ones)."""
     ids_block = np.ascontiguousarray(ids_block, dtype=np.int32)
     P, Q = _tensor(P, s), _tensor(Q, s)
+    g = _gate(gate, s.block, s)
     T = np.empty((s.block - 1, s.top_k, s.top_k))
     sh = _shape(s)
-    if load().orc_transitions(C.byref(sh), int(anchor), _p(ids_block), _p(P), _p(Q), _p(T)) != 0:
+    if load().orc_transitions(C.byref(sh), int(anchor), _p(ids_block), _p(P), _p(Q), _p(g), _p(T)) != 0:
         raise ValueError("orc_transitions rejected the shape")
     return T
 
@@ -126,15 +137,17 @@ def viterbi(logp_block: np.ndarray, T: np.ndarray):
     return idx, float(score[0]), float(margin[0])
 
 
-def draft_block(s, h, anchor, wg, W, P, Q):
-    """End-to-end oracle: dict(path, score, ids, logp, lse, idx, margin)."""
+def draft_block(s, h, anchor, wg, W, P, Q, gate=None):
+    """End-to-end oracle: dict(path, score, ids, logp, lse, idx, margin);
+    gate [rows, r] or None (all ones)."""
     h, wg, W, P, Q = (_tensor(a, s) for a in (h, wg, W, P, Q))
+    g = _gate(gate, s.rows, s)
     anchor = np.ascontiguousarray(anchor, dtype=np.int32)
     path = np.empty((s.batch, s.block), dtype=np.int32); score = np.empty(s.batch)
     ids = np.empty((s.rows, s.top_k), dtype=np.int32); logp = np.empty((s.rows, s.top_k))
     lse = np.empty(s.rows); idx = np.empty((s.batch, s.block), dtype=np.int32); margin = np.empty(s.batch)
     sh = _shape(s)
-    rc = load().orc_draft_block(C.byref(sh), _p(h), _p(anchor), _p(wg), _p(W), _p(P), _p(Q),
+    rc = load().orc_draft_block(C.byref(sh), _p(h), _p(anchor), _p(wg), _p(W), _p(P), _p(Q), _p(g),
                                 _p(path), _p(score), _p(ids), _p(logp), _p(lse), _p(idx), _p(margin))
     if rc != 0:
         raise ValueError("orc_draft_block failed")

@@ -209,11 +209,13 @@ int orc_head(const orc_shape* s, const void* y, const void* W, int r0, int nr,
 
 /* ---- step 7: low-rank adjacent-transition scores -------------------------- */
 /* Inco AI post, "lightweight path selector": the pair score of successor b
- * after predecessor a is <A(a), B(b)> (context gate taken as 1), A and B being
- * per-token rank-r embeddings; here P holds A(.) and Q holds B(.).  The first
- * draft slot follows the verified anchor. */
+ * after predecessor a at slot t is <A(a) (*) H(h_t), B(b)>, A and B being
+ * per-token rank-r embeddings and H(h_t) a context gate of slot t's hidden
+ * state (elementwise product).  Here P holds A(.), Q holds B(.) and gate row t
+ * holds H(h_t); with no gate, H = 1.  The first draft slot follows the
+ * verified anchor. */
 int orc_transitions(const orc_shape* s, int32_t anchor, const int32_t* ids,
-                    const void* P, const void* Q, double* T)
+                    const void* P, const void* Q, const double* gate, double* T)
 {
     const int B = s->block, K = s->top_k, r = s->rank;
     if (B < 2 || K <= 0) return -1;
@@ -226,7 +228,10 @@ int orc_transitions(const orc_shape* s, int32_t anchor, const int32_t* ids,
                 const int64_t a = (t == 1) ? anchor : ids[(t - 1) * K + j];
                 const int64_t b = ids[t * K + k];
                 double acc = 0.0;
-                for (int i = 0; i < r; ++i) acc += elem(s, P, a * r + i) * elem(s, Q, b * r + i);
+                for (int i = 0; i < r; ++i) {
+                    const double g = gate ? gate[(int64_t)t * r + i] : 1.0;
+                    acc += elem(s, P, a * r + i) * g * elem(s, Q, b * r + i);
+                }
                 Tt[j * K + k] = acc;
             }
         }
@@ -315,8 +320,8 @@ int orc_viterbi(int B, int K, const double* logp, const double* T,
 
 int orc_draft_block(const orc_shape* s, const void* h, const int32_t* anchor,
                     const void* wg, const void* W, const void* P, const void* Q,
-                    int32_t* path, double* score, int32_t* ids, double* logp,
-                    double* lse, int32_t* idx, double* margin)
+                    const double* gate, int32_t* path, double* score, int32_t* ids,
+                    double* logp, double* lse, int32_t* idx, double* margin)
 {
     const int B = s->block, K = s->top_k, D = s->hidden, V = s->vocab;
     const int rows = s->batch * B;
@@ -340,7 +345,8 @@ int orc_draft_block(const orc_shape* s, const void* h, const int32_t* anchor,
         if (anchor[b] < 0 || anchor[b] >= V) {
             for (int t = 0; t < B; ++t) { path[b * B + t] = -1; bi[t] = -1; }
         } else {
-            if (orc_transitions(s, anchor[b], cid + (int64_t)b * B * K, P, Q, T)) goto done;
+            const double* gb = gate ? gate + (int64_t)b * B * s->rank : NULL;
+            if (orc_transitions(s, anchor[b], cid + (int64_t)b * B * K, P, Q, gb, T)) goto done;
             if (orc_viterbi(B, K, clp + (int64_t)b * B * K, T, bi, &sc, &mg)) goto done;
             path[b * B] = anchor[b];
             for (int t = 1; t < B; ++t) path[b * B + t] = cid[((int64_t)b * B + t) * K + bi[t]];

@@ -76,10 +76,12 @@ int orc_topk(int nr, int V, int K, const double* logits,
              int32_t* ids, double* logp, double* lse);
 
 /* Transition scores of one block, C-def step 7.  ids [B][K] are the block's
- * candidates (row 0 ignored).  T [B-1][K][K]: T[t-1][j][k] = <P[prev_j], Q[ids[t][k]]>
+ * candidates (row 0 ignored).  gate [B][r] (nullable: all ones) holds the
+ * context gate of each slot (row 0 ignored).  T [B-1][K][K]:
+ * T[t-1][j][k] = sum_i P[prev_j][i] * gate[t][i] * Q[ids[t][k]][i]
  * with prev = {anchor} for t = 1 (only j = 0 is written; the rest are 0). */
 int orc_transitions(const orc_shape* s, int32_t anchor, const int32_t* ids,
-                    const void* P, const void* Q, double* T);
+                    const void* P, const void* Q, const double* gate, double* T);
 
 /* Best-path walk of one block, C-def step 8.  logp [B][K] (row 0 ignored),
  * T as above.  idx [B] receives idx[0] = -1 and the chosen candidate index of
@@ -89,14 +91,14 @@ int orc_viterbi(int B, int K, const double* logp, const double* T,
                 int32_t* idx, double* score, double* margin);
 
 /* Whole path for all blocks: conv, rounding of y to the dtype, head, top-K,
- * transitions and walk.  Outputs: path [batch][B] (slot 0 = anchor; -1 for
- * every slot of a block whose anchor is outside [0, V)), score [batch]
- * (NaN for such a block), and nullable ids [rows][K], logp [rows][K],
- * lse [rows], idx [batch][B], margin [batch]. */
+ * transitions (gate [rows][r], nullable: all ones) and walk.  Outputs: path
+ * [batch][B] (slot 0 = anchor; -1 for every slot of a block whose anchor is
+ * outside [0, V)), score [batch] (NaN for such a block), and nullable
+ * ids [rows][K], logp [rows][K], lse [rows], idx [batch][B], margin [batch]. */
 int orc_draft_block(const orc_shape* s, const void* h, const int32_t* anchor,
                     const void* wg, const void* W, const void* P, const void* Q,
-                    int32_t* path, double* score, int32_t* ids, double* logp,
-                    double* lse, int32_t* idx, double* margin);
+                    const double* gate, int32_t* path, double* score, int32_t* ids,
+                    double* logp, double* lse, int32_t* idx, double* margin);
 
 /* Number of OpenMP threads the oracle will use. */
 int orc_threads(void);

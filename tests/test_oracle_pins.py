@@ -248,6 +248,48 @@ def test_transitions_match_numpy(orc, dtype):
     assert not np.allclose(T_sw[1], T[1])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_transitions_gate(orc, dtype):
+    """Context gate H(h_t) of the Inco AI post's pair score
+    <A(a) (*) H(h_t), B(b)>: all-ones reproduces the ungated scores exactly;
+    a constant c_t in row t scales T_t (and only T_t) by c_t, which pins the
+    gate row to the successor's slot; a unit-vector gate e_i keeps the single
+    product P[a, i] * Q[b, i]."""
+    s = f32_shape(block=5, vocab=400, top_k=5, rank=16, dtype=dtype)
+    inp = wl.make_inputs_for(s, 41, parts=("P", "Q"))
+    P, Q = inp["P"], inp["Q"]
+    Pd = wl.bf16_bits_to_f32(P).astype(np.float64) if dtype == "bf16" else P.astype(np.float64)
+    Qd = wl.bf16_bits_to_f32(Q).astype(np.float64) if dtype == "bf16" else Q.astype(np.float64)
+    rng = np.random.default_rng(42)
+    ids = rng.integers(0, s.vocab, (s.block, s.top_k)).astype(np.int32)
+    anchor = 77
+    T = orc.transitions(s, anchor, ids, P, Q)
+    assert np.array_equal(orc.transitions(s, anchor, ids, P, Q, gate=np.ones((s.block, s.rank))), T)
+    c = np.array([100.0, 2.0, 0.5, -3.0, 0.25])  # row 0 (the anchor's slot) is never read
+    Tc = orc.transitions(s, anchor, ids, P, Q, gate=np.repeat(c[:, None], s.rank, axis=1))
+    for t in range(1, s.block):
+        np.testing.assert_allclose(Tc[t - 1], c[t] * T[t - 1], rtol=1e-13, atol=1e-14)
+    i = 7
+    e = np.zeros((s.block, s.rank))
+    e[:, i] = 1.0
+    Te = orc.transitions(s, anchor, ids, P, Q, gate=e)
+    assert Te[0, 0, 3] == Pd[anchor, i] * Qd[ids[1, 3], i]
+    for t in range(2, s.block):
+        for j in range(s.top_k):
+            for k in range(s.top_k):
+                assert Te[t - 1, j, k] == Pd[ids[t - 1, j], i] * Qd[ids[t, k], i]
+
+
+def test_draft_block_gate_ones_matches_ungated(orc):
+    s = wl.shape_of(0)
+    inp = wl.make_inputs(0)
+    a = orc.draft_block(s, inp["h"], inp["anchor"], inp["wg"], inp["W"], inp["P"], inp["Q"])
+    b = orc.draft_block(s, inp["h"], inp["anchor"], inp["wg"], inp["W"], inp["P"], inp["Q"],
+                        gate=np.ones((s.rows, s.rank)))
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
 # --------------------------------------------------------------------------- walk
 
 def brute_force(logp, T):
