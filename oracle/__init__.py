@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     topk,
     transitions,
     viterbi,
+    walk,
     draft_block,
     threads,
 )

@@ -32,6 +32,7 @@ def load():
         lib.orc_transitions.argtypes = [C.POINTER(_Shape), C.c_int32, P, P, P, P, P]
         lib.orc_viterbi.argtypes = [C.c_int, C.c_int, P, P, P, P, P]
         lib.orc_draft_block.argtypes = [C.POINTER(_Shape)] + [P] * 14
+        lib.orc_walk.argtypes = [C.c_int, C.c_int, P, P, C.c_int, C.c_double, P, P, P]
         lib.orc_threads.argtypes = []
         _LIB = lib
     return _LIB
@@ -135,6 +136,20 @@ def viterbi(logp_block: np.ndarray, T: np.ndarray):
     if load().orc_viterbi(B, K, _p(logp_block), _p(T), _p(idx), _p(score), _p(margin)) != 0:
         raise ValueError("orc_viterbi rejected the shape")
     return idx, float(score[0]), float(margin[0])
+
+
+def walk(logp_block: np.ndarray, T: np.ndarray, mode: str, temperature: float = 1.0, uniforms=None):
+    """Greedy ("greedy") or sampled ("sample") walk of one block: (idx [B]
+    with idx[0] = -1, score).  uniforms [B] (entry t for slot t)."""
+    logp_block = np.ascontiguousarray(logp_block, dtype=np.float64)
+    T = np.ascontiguousarray(T, dtype=np.float64)
+    B, K = logp_block.shape
+    m = {"greedy": 1, "sample": 2}[mode]
+    u = None if uniforms is None else np.ascontiguousarray(uniforms, dtype=np.float64)
+    idx = np.empty(B, dtype=np.int32); score = np.empty(1)
+    if load().orc_walk(B, K, _p(logp_block), _p(T), m, float(temperature), _p(u), _p(idx), _p(score)) != 0:
+        raise ValueError("orc_walk rejected the arguments")
+    return idx, float(score[0])
 
 
 def draft_block(s, h, anchor, wg, W, P, Q, gate=None):

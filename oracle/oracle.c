@@ -316,6 +316,55 @@ int orc_viterbi(int B, int K, const double* logp, const double* T,
     return 0;
 }
 
+/* ---- step 8, other walk rules ----------------------------------------------- */
+/* Inco AI post, "lightweight path selector": besides the best path, the
+ * selector can walk greedily, taking at each slot the best successor of the
+ * token chosen before it, or sample the successor from the same scores at a
+ * temperature.  Score of candidate k at slot t after index p of slot t-1:
+ * s_t(k) = logp[t][k] + T[t-1][p][k] (p = 0, the anchor, at t = 1).
+ *  greedy: the largest s_t(k), lowest k on ties;
+ *  sample: weights e_k = exp((s_t(k) - max_k s_t(k)) / temperature); with
+ *          prefix sums E_k = e_0 + ... + e_k in index order, the smallest k
+ *          with E_k > u_t * E_{K-1}, where u_t in [0, 1) is the caller's
+ *          uniform for slot t (uniforms[t], t >= 1).
+ * idx [B] receives -1 then the chosen indices; *score the sum of the chosen
+ * s_t. */
+int orc_walk(int B, int K, const double* logp, const double* T, int mode,
+             double temperature, const double* uniforms, int32_t* idx, double* score)
+{
+    if (B < 2 || K <= 0 || (mode != 1 && mode != 2)) return -1;
+    if (mode == 2 && (!uniforms || !(temperature > 0.0))) return -1;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)K);
+    double* pre = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!sc || !pre) { free(sc); free(pre); return -1; }
+    int prev = 0;
+    double total = 0.0;
+    idx[0] = -1;
+    for (int t = 1; t < B; ++t) {
+        const double* Tt = T + (int64_t)(t - 1) * K * K + (int64_t)prev * K;
+        double m = -INFINITY;
+        int best = 0;
+        for (int k = 0; k < K; ++k) {
+            sc[k] = logp[(int64_t)t * K + k] + Tt[k];
+            if (sc[k] > m) { m = sc[k]; best = k; }
+        }
+        int pick = best;
+        if (mode == 2) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) { acc += exp((sc[k] - m) / temperature); pre[k] = acc; }
+            const double target = uniforms[t] * acc;
+            pick = K - 1;
+            for (int k = 0; k < K; ++k) if (pre[k] > target) { pick = k; break; }
+        }
+        idx[t] = pick;
+        total += sc[pick];
+        prev = pick;
+    }
+    *score = total;
+    free(sc); free(pre);
+    return 0;
+}
+
 /* ---- the whole draft block ------------------------------------------------ */
 
 int orc_draft_block(const orc_shape* s, const void* h, const int32_t* anchor,

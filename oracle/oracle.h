@@ -90,6 +90,13 @@ int orc_transitions(const orc_shape* s, int32_t anchor, const int32_t* ids,
 int orc_viterbi(int B, int K, const double* logp, const double* T,
                 int32_t* idx, double* score, double* margin);
 
+/* Other walk rules of one block (mode 1 greedy, 2 sample), C-def step 8b.
+ * logp [B][K] and T as for orc_viterbi; uniforms [B] (mode 2; entry t is the
+ * uniform of slot t, entry 0 ignored).  Returns -1 for a bad mode or, in
+ * mode 2, a missing uniform vector or temperature <= 0. */
+int orc_walk(int B, int K, const double* logp, const double* T, int mode,
+             double temperature, const double* uniforms, int32_t* idx, double* score);
+
 /* Whole path for all blocks: conv, rounding of y to the dtype, head, top-K,
  * transitions (gate [rows][r], nullable: all ones) and walk.  Outputs: path
  * [batch][B] (slot 0 = anchor; -1 for every slot of a block whose anchor is

@@ -488,3 +488,75 @@ def test_draft_block_bad_anchor(orc):
     out = orc.draft_block(s, inp["h"], anchor, inp["wg"], inp["W"], inp["P"], inp["Q"])
     assert out["path"][0, 0] == anchor[0] and np.all(out["path"][0] >= 0)
     assert np.all(out["path"][1:] == -1) and np.all(np.isnan(out["score"][1:]))
+
+
+# --------------------------------------------------------------------------- other walk rules
+
+def test_greedy_zero_transitions_is_argmax(orc):
+    rng = np.random.default_rng(51)
+    lp = np.round(rng.standard_normal((6, 5)) * 4) / 4  # dyadic: exact ties happen
+    lp[3, 1] = lp[3, 4] = lp[3].max() + 1.0  # a tie for the maximum: the lower index wins
+    idx, sc = orc.walk(lp, np.zeros((5, 5, 5)), "greedy")
+    want = [int(np.argmax(lp[t])) for t in range(1, 6)]
+    assert list(idx) == [-1] + want and want[2] == 1
+    assert sc == sum(lp[t, want[t - 1]] for t in range(1, 6))
+
+
+def test_greedy_one_slot_is_viterbi(orc):
+    rng = np.random.default_rng(52)
+    lp = rng.standard_normal((2, 7))
+    T = rng.standard_normal((1, 7, 7))
+    gi, gs = orc.walk(lp, T, "greedy")
+    vi, vs, _ = orc.viterbi(lp, T)
+    assert list(gi) == list(vi) and gs == vs
+
+
+def test_greedy_is_myopic(orc):
+    """Closed form: the best first step leads into a heavily penalised pair,
+    which the best path avoids."""
+    lp = np.array([[0.0, 0.0], [0.0, -0.1], [0.0, 0.0]])
+    T = np.zeros((2, 2, 2))
+    T[1, 0, :] = -5.0
+    gi, gs = orc.walk(lp, T, "greedy")
+    vi, vs, _ = orc.viterbi(lp, T)
+    assert list(gi) == [-1, 0, 0] and gs == -5.0
+    assert list(vi) == [-1, 1, 0] and vs == -0.1
+
+
+def test_sample_uniform_scores_is_floor(orc):
+    K = 8
+    lp, T = np.zeros((2, K)), np.zeros((1, K, K))
+    for i in range(K):
+        for frac in (0.0, 0.3, 0.999):
+            u = (i + frac) / K
+            idx, _ = orc.walk(lp, T, "sample", 1.0, np.array([0.0, u]))
+            assert idx[1] == i
+
+
+def test_sample_tiny_temperature_is_greedy(orc):
+    rng = np.random.default_rng(53)
+    lp = rng.standard_normal((5, 6))
+    T = rng.standard_normal((4, 6, 6))
+    gi, gs = orc.walk(lp, T, "greedy")
+    for u in (0.0, 0.25, 0.5, 0.9):
+        si, ss = orc.walk(lp, T, "sample", 1e-9, np.full(5, u))
+        assert list(si) == list(gi) and ss == gs
+
+
+def test_sample_frequencies_follow_softmax(orc):
+    """With N evenly spaced uniforms, candidate k is picked for the uniforms
+    in [E_{k-1}, E_k) / E_{K-1}, so its count is N * softmax_k(s / temp) to
+    within one."""
+    rng = np.random.default_rng(54)
+    K, N, temp = 6, 1000, 0.7
+    lp = np.vstack([np.zeros(K), rng.standard_normal(K)])
+    T = rng.standard_normal((1, K, K))
+    s1 = lp[1] + T[0, 0]
+    p = np.exp((s1 - s1.max()) / temp)
+    p /= p.sum()
+    counts = np.zeros(K, int)
+    for i in range(N):
+        idx, sc = orc.walk(lp, T, "sample", temp, np.array([0.0, (i + 0.5) / N]))
+        counts[idx[1]] += 1
+        assert sc == s1[idx[1]]
+    assert np.all(np.abs(counts - N * p) <= 1.0)
