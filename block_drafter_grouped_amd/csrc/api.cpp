@@ -2,6 +2,8 @@
 // on the caller's stream.  No allocation, no synchronisation, no state.
 #include <stdint.h>
 
+#include <cmath>
+
 #include "../../include/dflash2.h"
 #include "kernels.h"
 
@@ -112,23 +114,40 @@ int dfs_topk_logits(const dfs_config* cfg, const float* logits, int32_t* cand_id
         dfs::launch_topk_logits(dims_of(cfg), logits, cand_ids, cand_logp, lse, (char*)ws, (hipStream_t)stream));
 }
 
-int dfs_select(const dfs_config* cfg, const int32_t* anchor, const int32_t* cand_ids, const float* cand_logp,
-               const void* P, const void* Q, int32_t* path, float* path_score, int32_t* path_idx, void* ws,
-               size_t ws_bytes, void* stream) {
+// Selector options: NULL means the best-path walk without a gate.
+int check_opts(const dfs_select_opts* o, dfs::SelectOpts* out) {
+    *out = dfs::SelectOpts{nullptr, DFS_WALK_VITERBI, 1.f, nullptr};
+    if (!o) return DFS_OK;
+    if (o->walk != DFS_WALK_VITERBI && o->walk != DFS_WALK_GREEDY && o->walk != DFS_WALK_SAMPLE)
+        return DFS_ERR_UNSUPPORTED;
+    if (o->walk == DFS_WALK_SAMPLE) {
+        if (!o->uniforms) return DFS_ERR_NULL;
+        if (!(o->temperature > 0.f) || !std::isfinite(o->temperature)) return DFS_ERR_SHAPE;
+    }
+    if (misaligned(o->gate, 16) || misaligned(o->uniforms, 16)) return DFS_ERR_MISALIGNED;
+    *out = dfs::SelectOpts{o->gate, o->walk, o->temperature, o->walk == DFS_WALK_SAMPLE ? o->uniforms : nullptr};
+    return DFS_OK;
+}
+
+int dfs_select(const dfs_config* cfg, const dfs_select_opts* opts, const int32_t* anchor, const int32_t* cand_ids,
+               const float* cand_logp, const void* P, const void* Q, int32_t* path, float* path_score,
+               int32_t* path_idx, void* ws, size_t ws_bytes, void* stream) {
     int st = check_cfg(cfg);
     if (st) return st;
     if (!anchor || !cand_ids || !cand_logp || !P || !Q || !path || !path_score) return DFS_ERR_NULL;
     if (misaligned(anchor, 16) || misaligned(cand_ids, 16) || misaligned(cand_logp, 16) || misaligned(P, 16) ||
         misaligned(Q, 16) || misaligned(path, 16) || misaligned(path_score, 16) || misaligned(path_idx, 16))
         return DFS_ERR_MISALIGNED;
+    dfs::SelectOpts o;
+    if ((st = check_opts(opts, &o))) return st;
     if ((st = check_ws(cfg, ws, ws_bytes))) return st;
-    return hip_status(dfs::launch_select(dims_of(cfg), anchor, cand_ids, cand_logp, P, Q, path, path_score, path_idx,
-                                         (char*)ws, (hipStream_t)stream));
+    return hip_status(dfs::launch_select(dims_of(cfg), o, anchor, cand_ids, cand_logp, P, Q, path, path_score,
+                                         path_idx, (char*)ws, (hipStream_t)stream));
 }
 
-int dfs_draft_block(const dfs_config* cfg, const void* h, const int32_t* anchor, const void* wg_cm, const void* W,
-                    const void* P, const void* Q, int32_t* path, float* path_score, int32_t* cand_ids,
-                    float* cand_logp, void* ws, size_t ws_bytes, void* stream) {
+int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts, const void* h, const int32_t* anchor,
+                    const void* wg_cm, const void* W, const void* P, const void* Q, int32_t* path, float* path_score,
+                    int32_t* cand_ids, float* cand_logp, void* ws, size_t ws_bytes, void* stream) {
     int st = check_cfg(cfg);
     if (st) return st;
     if (!h || !anchor || !wg_cm || !W || !P || !Q || !path || !path_score) return DFS_ERR_NULL;
@@ -136,6 +155,8 @@ int dfs_draft_block(const dfs_config* cfg, const void* h, const int32_t* anchor,
         misaligned(P, 16) || misaligned(Q, 16) || misaligned(path, 16) || misaligned(path_score, 16) ||
         misaligned(cand_ids, 16) || misaligned(cand_logp, 16))
         return DFS_ERR_MISALIGNED;
+    dfs::SelectOpts o;
+    if ((st = check_opts(opts, &o))) return st;
     if ((st = check_ws(cfg, ws, ws_bytes))) return st;
     const Dims d = dims_of(cfg);
     const dfs::WsLayout L = dfs::ws_layout(d);
@@ -147,7 +168,7 @@ int dfs_draft_block(const dfs_config* cfg, const void* h, const int32_t* anchor,
     float* lse = (float*)(w + L.lse);
     if ((st = hip_status(dfs::launch_conv(d, h, wg_cm, y, nullptr, w, s)))) return st;
     if ((st = hip_status(dfs::launch_head_topk(d, y, W, cids, clogp, lse, nullptr, w, s)))) return st;
-    return hip_status(dfs::launch_select(d, anchor, cids, clogp, P, Q, path, path_score, nullptr, w, s));
+    return hip_status(dfs::launch_select(d, o, anchor, cids, clogp, P, Q, path, path_score, nullptr, w, s));
 }
 
 }  // extern "C"

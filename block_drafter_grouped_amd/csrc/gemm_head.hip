@@ -213,15 +213,32 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
     }
 }
 
-// fp32 correctness path: plain dot products, logits written out.
+// fp32 path: plain dot products, logits written out.  A thread owns one
+// vocabulary row and walks it in 16-B pieces against up to 8 hidden rows at a
+// time (the hidden-row addresses are uniform across the wave, so those loads
+// are shared); the loads of several pieces are in flight together.
 __global__ __launch_bounds__(256) void head_f32_kernel(const float* __restrict__ y, const float* __restrict__ W,
                                                        float* __restrict__ logits, int rows, int D, int V) {
     const int v = blockIdx.x * blockDim.x + threadIdx.x;
     if (v >= V) return;
-    for (int row = 0; row < rows; ++row) {
-        float acc = 0.f;
-        for (int c = 0; c < D; ++c) acc += y[(size_t)row * D + c] * W[(size_t)v * D + c];
-        logits[(size_t)row * V + v] = acc;
+    const float* wr = W + (size_t)v * D;
+    for (int r0 = 0; r0 < rows; r0 += 8) {
+        const int nr = min(8, rows - r0);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int c = 0; c < D; c += 4) {
+            const f32x4 w = *(const f32x4*)(wr + c);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (r < nr) {
+                    const f32x4 x = *(const f32x4*)(y + (size_t)(r0 + r) * D + c);
+                    acc[r] += x[0] * w[0] + x[1] * w[1] + x[2] * w[2] + x[3] * w[3];
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (r < nr) logits[(size_t)(r0 + r) * V + v] = acc[r];
     }
 }
 

@@ -63,8 +63,17 @@ hipError_t launch_logits_partials(const Dims& d, const float* logits, int nsl, u
 hipError_t launch_topk_logits(const Dims& d, const float* logits, int32_t* cand_ids, float* cand_logp,
                               float* lse, char* ws, hipStream_t s);
 
-hipError_t launch_select(const Dims& d, const int32_t* anchor, const int32_t* cand_ids,
-                         const float* cand_logp, const void* P, const void* Q, int32_t* path,
-                         float* path_score, int32_t* path_idx, char* ws, hipStream_t s);
+// Selector options: context gate [rows, r] (nullable: all ones); walk 0 best
+// path, 1 greedy, 2 sample (temperature, uniforms [batch, B]).
+struct SelectOpts {
+    const float* gate;
+    int walk;
+    float temperature;
+    const float* uniforms;
+};
+
+hipError_t launch_select(const Dims& d, const SelectOpts& o, const int32_t* anchor, const int32_t* cand_ids,
+                         const float* cand_logp, const void* P, const void* Q, int32_t* path, float* path_score,
+                         int32_t* path_idx, char* ws, hipStream_t s);
 
 }  // namespace dfs

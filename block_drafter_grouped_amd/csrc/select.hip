@@ -6,7 +6,8 @@
 // starts from the last verified token, as in the vLLM release-note article,
 // section "two additions").  The context gate of the post is taken as 1.
 //
-// Fast path (bf16 tables, K <= 16): select_fused_kernel, below.  General path:
+// Fast path (bf16 tables, K <= 16, no gate, best-path walk): select_fused_kernel,
+// below.  General path:
 // sel_dots: one workgroup per (draft slot, block) computes the K x K matrix
 //   T_t[j, k] = <P[c_{t-1, j}], Q[c_{t, k}]>   (c_0 = {anchor}: a 1 x K row)
 // from rows gathered out of P and Q, fp32 accumulation.
@@ -44,8 +45,8 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&out)[8]) {
 template <typename T>
 __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict__ anchor,
                                                        const int32_t* __restrict__ cand_ids, const T* __restrict__ P,
-                                                       const T* __restrict__ Q, float* __restrict__ Tout, int B, int K,
-                                                       int r, int V) {
+                                                       const T* __restrict__ Q, const float* __restrict__ gate,
+                                                       float* __restrict__ Tout, int B, int K, int r, int V) {
     const int t = blockIdx.x + 1, b = blockIdx.y;
     const int a = anchor[b];
     if (a < 0 || a >= V) return;
@@ -58,12 +59,24 @@ __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict
         if (pa >= 0 && pa < V && qb >= 0 && qb < V) {
             const T* pr = P + (size_t)pa * r;
             const T* qr = Q + (size_t)qb * r;
-            for (int i = 0; i < r; i += 8) {
-                float x[8], z[8];
-                load8<T>(pr + i, x);
-                load8<T>(qr + i, z);
+            if (gate) {  // context gate of slot t: (P * H) . Q
+                const float* gr = gate + ((size_t)b * B + t) * r;
+                for (int i = 0; i < r; i += 8) {
+                    float x[8], z[8], g[8];
+                    load8<T>(pr + i, x);
+                    load8<T>(qr + i, z);
+                    load8<float>(gr + i, g);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc += x[e] * z[e];
+                    for (int e = 0; e < 8; ++e) acc += (x[e] * g[e]) * z[e];
+                }
+            } else {
+                for (int i = 0; i < r; i += 8) {
+                    float x[8], z[8];
+                    load8<T>(pr + i, x);
+                    load8<T>(qr + i, z);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc += x[e] * z[e];
+                }
             }
         }
         Tout[(((size_t)b * (B - 1) + t - 1) * K + j) * K + k] = acc;
@@ -132,6 +145,73 @@ __global__ __launch_bounds__(kWave) void viterbi_kernel(const int32_t* __restric
         path[(size_t)b * B] = a;
         if (path_idx) path_idx[(size_t)b * B] = -1;
         path_score[b] = mx;
+    }
+}
+
+// The greedy and sampled walks (Inco AI post, "lightweight path selector":
+// take the best successor of the token chosen before, or sample it from the
+// same scores).  One wavefront per block, lane k = candidate k.  At slot t,
+// after index p of slot t-1 (p = 0, the anchor, at t = 1), candidate k
+// scores s_k = cand_logp[t][k] + T_t[p][k].  Greedy: the largest s_k, the
+// lowest k on ties.  Sample: e_k = exp((s_k - max s) / temperature), prefix
+// sums E_k in lane order, and the smallest k with E_k > u_t * E_{K-1} (the
+// last candidate if rounding leaves none), u_t = uniforms[b, t].  Each
+// decision follows the same rule as the fp64 reference, in fp32.
+__global__ __launch_bounds__(kWave) void walk_kernel(const int32_t* __restrict__ anchor,
+                                                     const int32_t* __restrict__ cand_ids,
+                                                     const float* __restrict__ cand_logp, const float* __restrict__ Tin,
+                                                     int sample, float temperature, const float* __restrict__ uniforms,
+                                                     int32_t* __restrict__ path, float* __restrict__ path_score,
+                                                     int32_t* __restrict__ path_idx, int B, int K, int V) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int a = anchor[b];
+    bool bad = (a < 0 || a >= V);
+    for (int i = lane; i < (B - 1) * K; i += kWave) {
+        const int id = cand_ids[((size_t)b * B + 1) * K + i];
+        bad |= (id < 0 || id >= V);
+    }
+    if (__any(bad)) {
+        for (int t = lane; t < B; t += kWave) {
+            path[(size_t)b * B + t] = -1;
+            if (path_idx) path_idx[(size_t)b * B + t] = -1;
+        }
+        if (lane == 0) path_score[b] = __int_as_float(0x7FC00000);
+        return;
+    }
+    const float* Tb = Tin + (size_t)b * (B - 1) * K * K;
+    const bool on = lane < K;
+    const float inv_t = 1.f / temperature;
+    int prev = 0;
+    float total = 0.f;
+    for (int t = 1; t < B; ++t) {
+        const float sk = on ? cand_logp[((size_t)b * B + t) * K + lane] + Tb[((size_t)(t - 1) * K + prev) * K + lane]
+                            : -INFINITY;
+        const float m = wave_max_f32(sk);
+        int pick;
+        if (!sample) {
+            pick = __ffsll((unsigned long long)__ballot(on && sk == m)) - 1;
+        } else {
+            float e = on ? __expf((sk - m) * inv_t) : 0.f;
+            for (int o = 1; o < kWave; o <<= 1) {  // inclusive prefix sum in lane order
+                const float v = __shfl_up(e, o, kWave);
+                if (lane >= o) e += v;
+            }
+            const float tot = readlane_f32(e, K - 1);
+            const float target = uniforms[(size_t)b * B + t] * tot;
+            const uint64_t over = __ballot(on && e > target);
+            pick = over ? __ffsll((unsigned long long)over) - 1 : K - 1;
+        }
+        total += readlane_f32(sk, pick);
+        prev = pick;
+        if (lane == 0) {
+            path[(size_t)b * B + t] = cand_ids[((size_t)b * B + t) * K + pick];
+            if (path_idx) path_idx[(size_t)b * B + t] = pick;
+        }
+    }
+    if (lane == 0) {
+        path[(size_t)b * B] = a;
+        if (path_idx) path_idx[(size_t)b * B] = -1;
+        path_score[b] = total;
     }
 }
 
@@ -251,10 +331,11 @@ __global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
 
 }  // namespace
 
-hipError_t launch_select(const Dims& d, const int32_t* anchor, const int32_t* cand_ids, const float* cand_logp,
-                         const void* P, const void* Q, int32_t* path, float* path_score, int32_t* path_idx, char* ws,
-                         hipStream_t s) {
-    if (d.bf16 && d.K <= 16 && d.r % 32 == 0) {
+hipError_t launch_select(const Dims& d, const SelectOpts& o, const int32_t* anchor, const int32_t* cand_ids,
+                         const float* cand_logp, const void* P, const void* Q, int32_t* path, float* path_score,
+                         int32_t* path_idx, char* ws, hipStream_t s) {
+    const bool plain = !o.gate && o.walk == 0;
+    if (plain && d.bf16 && d.K <= 16 && d.r % 32 == 0) {
         const size_t lds = (size_t)(d.B - 1) * 16 * 16 * sizeof(float);
         hipError_t e = hipFuncSetAttribute((const void*)select_fused_kernel<8>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -268,14 +349,17 @@ hipError_t launch_select(const Dims& d, const int32_t* anchor, const int32_t* ca
     float* T = (float*)(ws + L.T);
     dim3 grid(d.B - 1, d.batch);
     if (d.bf16)
-        sel_dots_kernel<uint16_t><<<grid, 256, 0, s>>>(anchor, cand_ids, (const uint16_t*)P, (const uint16_t*)Q, T,
-                                                       d.B, d.K, d.r, d.V);
+        sel_dots_kernel<uint16_t><<<grid, 256, 0, s>>>(anchor, cand_ids, (const uint16_t*)P, (const uint16_t*)Q,
+                                                       o.gate, T, d.B, d.K, d.r, d.V);
     else
-        sel_dots_kernel<float><<<grid, 256, 0, s>>>(anchor, cand_ids, (const float*)P, (const float*)Q, T, d.B, d.K,
-                                                    d.r, d.V);
+        sel_dots_kernel<float><<<grid, 256, 0, s>>>(anchor, cand_ids, (const float*)P, (const float*)Q, o.gate, T,
+                                                    d.B, d.K, d.r, d.V);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d.K <= 16)
+    if (o.walk != 0)
+        walk_kernel<<<d.batch, kWave, 0, s>>>(anchor, cand_ids, cand_logp, T, o.walk == 2, o.temperature, o.uniforms,
+                                              path, path_score, path_idx, d.B, d.K, d.V);
+    else if (d.K <= 16)
         viterbi_kernel<16><<<d.batch, kWave, 0, s>>>(anchor, cand_ids, cand_logp, T, path, path_score, path_idx, d.B,
                                                      d.K, d.V);
     else

@@ -46,6 +46,21 @@ class Config(C.Structure):
         return self.batch * self.block_size
 
 
+WALKS = {"viterbi": 0, "greedy": 1, "sample": 2}
+
+
+class SelectOpts(C.Structure):
+    """dfs_select_opts: context gate, walk rule, temperature, uniforms."""
+    _fields_ = [("gate", C.c_void_p), ("walk", C.c_int32), ("temperature", C.c_float),
+                ("uniforms", C.c_void_p)]
+
+
+def _opts(gate, walk, temperature, uniforms):
+    if gate is None and walk == "viterbi" and uniforms is None:
+        return None
+    return C.byref(SelectOpts(_ptr(gate), WALKS[walk], float(temperature), _ptr(uniforms)))
+
+
 class DFSError(RuntimeError):
     def __init__(self, status: int, fn: str):
         self.status = status
@@ -74,8 +89,8 @@ def _load():
     lib_.dfs_conv.argtypes = [cfg, P, P, P, P, P, S, P]
     lib_.dfs_head_topk.argtypes = [cfg, P, P, P, P, P, P, P, S, P]
     lib_.dfs_topk_logits.argtypes = [cfg, P, P, P, P, P, S, P]
-    lib_.dfs_select.argtypes = [cfg, P, P, P, P, P, P, P, P, P, S, P]
-    lib_.dfs_draft_block.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib_.dfs_select.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib_.dfs_draft_block.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     for n in EXPORTS[2:]:
         getattr(lib_, n).restype = I
     return lib_
@@ -138,14 +153,16 @@ def topk_logits(cfg, logits, cand_ids, cand_logp, lse, ws, stream=None):
                                 _ptr(ws), _nbytes(ws), _stream(stream)), "dfs_topk_logits")
 
 
-def select(cfg, anchor, cand_ids, cand_logp, P, Q, path, path_score, ws, path_idx=None, stream=None):
-    _check(_lib.dfs_select(C.byref(cfg), _ptr(anchor), _ptr(cand_ids), _ptr(cand_logp), _ptr(P), _ptr(Q),
-                           _ptr(path), _ptr(path_score), _ptr(path_idx), _ptr(ws), _nbytes(ws),
-                           _stream(stream)), "dfs_select")
+def select(cfg, anchor, cand_ids, cand_logp, P, Q, path, path_score, ws, path_idx=None, stream=None,
+           gate=None, walk="viterbi", temperature=1.0, uniforms=None):
+    _check(_lib.dfs_select(C.byref(cfg), _opts(gate, walk, temperature, uniforms), _ptr(anchor), _ptr(cand_ids),
+                           _ptr(cand_logp), _ptr(P), _ptr(Q), _ptr(path), _ptr(path_score), _ptr(path_idx),
+                           _ptr(ws), _nbytes(ws), _stream(stream)), "dfs_select")
 
 
 def draft_block(cfg, h, anchor, wg_cm, W, P, Q, path, path_score, ws, cand_ids=None, cand_logp=None,
-                stream=None):
-    _check(_lib.dfs_draft_block(C.byref(cfg), _ptr(h), _ptr(anchor), _ptr(wg_cm), _ptr(W), _ptr(P), _ptr(Q),
-                                _ptr(path), _ptr(path_score), _ptr(cand_ids), _ptr(cand_logp), _ptr(ws),
-                                _nbytes(ws), _stream(stream)), "dfs_draft_block")
+                stream=None, gate=None, walk="viterbi", temperature=1.0, uniforms=None):
+    _check(_lib.dfs_draft_block(C.byref(cfg), _opts(gate, walk, temperature, uniforms), _ptr(h), _ptr(anchor),
+                                _ptr(wg_cm), _ptr(W), _ptr(P), _ptr(Q), _ptr(path), _ptr(path_score),
+                                _ptr(cand_ids), _ptr(cand_logp), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "dfs_draft_block")

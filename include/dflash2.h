@@ -150,6 +150,33 @@ int dfs_topk_logits(const dfs_config* cfg, const float* logits,
                     int32_t* cand_ids, float* cand_logp, float* lse,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Walk rules of the selector (Inco AI post, "lightweight path selector"). */
+typedef enum {
+    DFS_WALK_VITERBI = 0, /* the best path: max over all paths (default)         */
+    DFS_WALK_GREEDY = 1,  /* at each slot, the best successor of the last choice */
+    DFS_WALK_SAMPLE = 2   /* at each slot, a successor sampled from the scores   */
+} dfs_walk;
+
+/*
+ * Selector options.  A NULL pointer means: no gate, DFS_WALK_VITERBI.
+ *  gate        [rows, r] fp32 device, nullable: the context gate H(h_t) of
+ *              each row (row b*B + t gates the transitions into slot t; the
+ *              Inco AI post's pair score <A(a) * H(h_t), B(b)>).  NULL: all
+ *              ones.  The pages give no form for H; the caller computes it.
+ *  walk        dfs_walk.
+ *  temperature DFS_WALK_SAMPLE: > 0 and finite (else DFS_ERR_SHAPE).
+ *  uniforms    DFS_WALK_SAMPLE: [batch, B] fp32 device (else DFS_ERR_NULL):
+ *              uniforms[b, t] in [0, 1) draws slot t of block b; column 0 is
+ *              not read.  The library draws no random numbers itself.
+ * Gated or non-Viterbi calls run the fp32 general selector kernels.
+ */
+typedef struct {
+    const float* gate;
+    int32_t walk;
+    float temperature;
+    const float* uniforms;
+} dfs_select_opts;
+
 /*
  * Steps 4-5: transition scores and the best path (Inco AI post, section
  * "lightweight path selector": every adjacent candidate pair is scored at
@@ -158,11 +185,18 @@ int dfs_topk_logits(const dfs_config* cfg, const float* logits,
  *
  * For block b with candidates c_t = cand_ids[b*B + t, :] (t >= 1) and
  * c_0 = {anchor[b]}:
- *   T_t[j, k] = sum_i P[c_{t-1, j}, i] * Q[c_{t, k}, i]      (fp32 accumulation)
+ *   T_t[j, k] = sum_i P[c_{t-1, j}, i] * H_t[i] * Q[c_{t, k}, i]   (fp32 accumulation;
+ *               H_t = gate row b*B + t, or 1)
  *   delta_1[k] = cand_logp[b*B+1, k] + T_1[0, k]
  *   delta_t[k] = max_j (delta_{t-1}[j] + T_t[j, k]) + cand_logp[b*B+t, k]
- * The path takes argmax_k delta_{B-1}[k] and backtracks; ties go to the
- * lowest index at every step.
+ * DFS_WALK_VITERBI: the path takes argmax_k delta_{B-1}[k] and backtracks;
+ * ties go to the lowest index at every step; path_score = delta_{B-1}.
+ * DFS_WALK_GREEDY / DFS_WALK_SAMPLE: from p_0 = the anchor, slot t scores
+ * s_t[k] = cand_logp[b*B+t, k] + T_t[p_{t-1}, k]; greedy takes the largest
+ * (lowest k on ties); sampling takes the smallest k whose prefix sum of
+ * exp((s_t - max s_t) / temperature), in index order, exceeds
+ * uniforms[b, t] times the total (the last k if none).  path_score is the
+ * sum of the chosen s_t.
  *
  *  anchor     [batch]     int32, the verified token of each block
  *  cand_ids   [rows, K]   int32, cand_logp [rows, K] fp32 (rows of slot 0 are
@@ -177,8 +211,8 @@ int dfs_topk_logits(const dfs_config* cfg, const float* logits,
  * A block whose anchor lies outside [0, V) gets path = -1 in every slot,
  * path_idx = -1 and path_score = NaN; the other blocks are unaffected.
  */
-int dfs_select(const dfs_config* cfg, const int32_t* anchor,
-               const int32_t* cand_ids, const float* cand_logp,
+int dfs_select(const dfs_config* cfg, const dfs_select_opts* opts,
+               const int32_t* anchor, const int32_t* cand_ids, const float* cand_logp,
                const void* P, const void* Q, int32_t* path, float* path_score,
                int32_t* path_idx, void* ws, size_t ws_bytes, void* stream);
 
@@ -187,7 +221,8 @@ int dfs_select(const dfs_config* cfg, const int32_t* anchor,
  * cand_ids / cand_logp are optional outputs (NULL: kept in the workspace).
  * Arguments as above.
  */
-int dfs_draft_block(const dfs_config* cfg, const void* h, const int32_t* anchor,
+int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts,
+                    const void* h, const int32_t* anchor,
                     const void* wg_cm, const void* W, const void* P, const void* Q,
                     int32_t* path, float* path_score, int32_t* cand_ids,
                     float* cand_logp, void* ws, size_t ws_bytes, void* stream);

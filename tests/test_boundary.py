@@ -149,34 +149,67 @@ def test_topk_logits_validation():
 def test_select_validation():
     c = cfg_of(3)
     ws = dfs.workspace_size(c)
-    base = [C.byref(c), A, A, A, A, A, A, A, None, A, ws, None]
-    for i in (1, 2, 3, 4, 5, 6, 7, 9):
+    base = [C.byref(c), None, A, A, A, A, A, A, A, None, A, ws, None]
+    for i in (2, 3, 4, 5, 6, 7, 8, 10):
         a = list(base)
         a[i] = None
         assert L.dfs_select(*a) == NULL, i
-    for i in (1, 2, 3, 4, 5, 6, 7, 8):
+    for i in (2, 3, 4, 5, 6, 7, 8, 9):
         a = list(base)
         a[i] = A + 8
         assert L.dfs_select(*a) == MISAL, i
     a = list(base)
-    a[10] = 16
+    a[11] = 16
     assert L.dfs_select(*a) == WS
+
+
+def opts(**kw):
+    o = dfs.dflash2.SelectOpts(None, 0, 1.0, None)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return C.byref(o)
+
+
+@pytest.mark.parametrize("o,status", [
+    (dict(walk=3), UNSUP), (dict(walk=-1), UNSUP),
+    (dict(walk=2), NULL),                                   # sampling needs the uniforms
+    (dict(walk=2, uniforms=A, temperature=0.0), SHAPE),
+    (dict(walk=2, uniforms=A, temperature=-1.0), SHAPE),
+    (dict(walk=2, uniforms=A, temperature=float("inf")), SHAPE),
+    (dict(walk=2, uniforms=A, temperature=float("nan")), SHAPE),
+    (dict(walk=2, uniforms=A + 4), MISAL),
+    (dict(gate=A + 8), MISAL),
+])
+def test_select_options_validation(o, status):
+    c = cfg_of(3)
+    ws = dfs.workspace_size(c)
+    assert L.dfs_select(C.byref(c), opts(**o), A, A, A, A, A, A, A, None, A, ws, None) == status
+    assert L.dfs_draft_block(C.byref(c), opts(**o), A, A, A, A, A, A, A, A, None, None, A, ws, None) == status
+
+
+def test_select_options_unused_fields_ignored():
+    """Uniforms and temperature are read only by the sampling walk: a greedy
+    call with a bad temperature and no uniforms is still valid (it reaches
+    the workspace check, the last host-side rule)."""
+    c = cfg_of(3)
+    o = opts(walk=1, temperature=0.0)
+    assert L.dfs_select(C.byref(c), o, A, A, A, A, A, A, A, None, A, 16, None) == WS
 
 
 def test_draft_block_validation():
     c = cfg_of(2)
     ws = dfs.workspace_size(c)
-    base = [C.byref(c), A, A, A, A, A, A, A, A, None, None, A, ws, None]
-    for i in (1, 2, 3, 4, 5, 6, 7, 8, 11):
+    base = [C.byref(c), None, A, A, A, A, A, A, A, A, None, None, A, ws, None]
+    for i in (2, 3, 4, 5, 6, 7, 8, 9, 12):
         a = list(base)
         a[i] = None
         assert L.dfs_draft_block(*a) == NULL, i
-    for i in (1, 2, 3, 4, 5, 6, 7, 8, 9, 10):
+    for i in (2, 3, 4, 5, 6, 7, 8, 9, 10, 11):
         a = list(base)
         a[i] = A + 2
         assert L.dfs_draft_block(*a) == MISAL, i
     a = list(base)
-    a[12] = ws // 2
+    a[13] = ws // 2
     assert L.dfs_draft_block(*a) == WS
     assert L.dfs_draft_block(C.byref(cfg_of(2, block_size=1)), *base[1:]) == SHAPE
 

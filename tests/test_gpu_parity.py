@@ -329,6 +329,141 @@ def test_select_figure1_repetition():
     assert score[0] == g["expected_score"]
 
 
+# ============================================================== selector options (gate, walks)
+
+GATE_SHAPES = [
+    S(batch=4, block=8, vocab=5000, top_k=16, rank=256),           # bf16, K 16: leaves the fused kernel
+    S(batch=3, block=5, vocab=4000, top_k=33, rank=8),             # general path
+    S(batch=5, block=16, vocab=2000, top_k=16, rank=256, dtype="f32"),
+]
+
+
+def gate_for(s, seed):
+    rng = np.random.default_rng(seed)
+    return (0.5 + rng.random((s.rows, s.rank))).astype(np.float32)
+
+
+def run_select_opts(s, ids, lp, P, Q, anchor, **opts):
+    cfg = dfs.Config.of(s)
+    path = empty((s.batch, s.block), torch.int32)
+    score = empty((s.batch,), torch.float32)
+    pidx = empty((s.batch, s.block), torch.int32)
+    o = {k: (to_dev(v) if isinstance(v, np.ndarray) else v) for k, v in opts.items()}
+    dfs.select(cfg, to_dev(anchor), to_dev(ids), to_dev(lp), to_dev(P), to_dev(Q), path, score, wsbuf(cfg),
+               path_idx=pidx, **o)
+    torch.cuda.synchronize()
+    return from_dev(path), from_dev(score), from_dev(pidx)
+
+
+def block_T(s, ids, P, Q, anchor, b, gate=None):
+    rs = slice(b * s.block, (b + 1) * s.block)
+    return orc.transitions(s, int(anchor[b]), ids[rs], P, Q, gate=None if gate is None else gate[rs])
+
+
+@pytest.mark.parametrize("s", GATE_SHAPES, ids=str)
+def test_select_gated_fed(s):
+    ids, lp, P, Q, anchor = select_inputs(s, 61 + s.block)
+    gate = gate_for(s, 62)
+    path, score, pidx = run_select_opts(s, ids, lp, P, Q, anchor, gate=gate)
+    for b in range(s.batch):
+        rs = slice(b * s.block, (b + 1) * s.block)
+        T = block_T(s, ids, P, Q, anchor, b, gate)
+        idx, sc, margin = orc.viterbi(lp[rs].astype(np.float64), T)
+        if margin > NEAR_TIE:
+            assert list(pidx[b]) == list(idx)
+            assert abs(score[b] - sc) <= SCORE_TOL
+        assert path[b, 0] == anchor[b]
+        assert all(path[b, t] == ids[b * s.block + t, pidx[b, t]] for t in range(1, s.block))
+
+
+def test_select_gate_ones():
+    """All-ones gate: bit-identical to no gate on the general path; the
+    same paths as the fused kernel where they are not near ties."""
+    s = S(batch=3, block=5, vocab=4000, top_k=33, rank=8)
+    ids, lp, P, Q, anchor = select_inputs(s, 71)
+    ones = np.ones((s.rows, s.rank), np.float32)
+    a = run_select(s, ids, lp, P, Q, anchor)
+    b = run_select_opts(s, ids, lp, P, Q, anchor, gate=ones)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    s = S(batch=4, block=8, vocab=5000, top_k=16, rank=256)
+    ids, lp, P, Q, anchor = select_inputs(s, 72)
+    a = run_select(s, ids, lp, P, Q, anchor)
+    b = run_select_opts(s, ids, lp, P, Q, anchor, gate=np.ones((s.rows, s.rank), np.float32))
+    for blk in range(s.batch):
+        _, _, margin = oracle_walk(s, ids, lp, P, Q, anchor, blk)
+        if margin > NEAR_TIE:
+            assert list(a[2][blk]) == list(b[2][blk])
+        assert abs(a[1][blk] - b[1][blk]) <= SCORE_TOL
+
+
+def check_walk(s, ids, lp, P, Q, anchor, pidx, score, walk, temperature=1.0, uniforms=None, gate=None):
+    """The GPU walk agrees with the oracle walk slot by slot.  At a slot where
+    the two choose differently, the fp64 scores must make it a near tie
+    (greedy) or put the uniform within 1e-5 of the boundary between the two
+    choices (sampling); the rest of that block then follows another
+    predecessor and is not compared."""
+    for b in range(s.batch):
+        rs = slice(b * s.block, (b + 1) * s.block)
+        T = block_T(s, ids, P, Q, anchor, b, gate)
+        lpb = lp[rs].astype(np.float64)
+        u = None if uniforms is None else uniforms[b].astype(np.float64)
+        idx, sc = orc.walk(lpb, T, walk, temperature, u)
+        prev, same = 0, True
+        for t in range(1, s.block):
+            sk = lpb[t] + T[t - 1, prev]
+            g, o = int(pidx[b, t]), int(idx[t])
+            if g != o:
+                if walk == "greedy":
+                    assert abs(sk[g] - sk[o]) <= SCORE_TOL, (b, t)
+                else:
+                    e = np.exp((sk - sk.max()) / temperature)
+                    cdf = np.cumsum(e) / e.sum()
+                    edge = cdf[min(g, o)]
+                    assert abs(u[t] - edge) <= 1e-5, (b, t, u[t], edge)
+                same = False
+                break
+            prev = g
+        if same:
+            assert abs(score[b] - sc) <= SCORE_TOL, b
+
+
+@pytest.mark.parametrize("s", SELECT_SHAPES[:4] + GATE_SHAPES[2:], ids=str)
+def test_select_greedy_fed(s):
+    ids, lp, P, Q, anchor = select_inputs(s, 81 + s.block)
+    path, score, pidx = run_select_opts(s, ids, lp, P, Q, anchor, walk="greedy")
+    assert np.all(path[:, 0] == anchor) and np.all(pidx[:, 0] == -1)
+    check_walk(s, ids, lp, P, Q, anchor, pidx, score, "greedy")
+
+
+@pytest.mark.parametrize("temperature", [0.5, 1.0, 3.0])
+@pytest.mark.parametrize("s", [SELECT_SHAPES[0], SELECT_SHAPES[3], GATE_SHAPES[2]], ids=str)
+def test_select_sample_fed(s, temperature):
+    ids, lp, P, Q, anchor = select_inputs(s, 91 + s.block)
+    u = np.random.default_rng(92).random((s.batch, s.block)).astype(np.float32)
+    gate = gate_for(s, 93)
+    path, score, pidx = run_select_opts(s, ids, lp, P, Q, anchor, walk="sample", temperature=temperature,
+                                        uniforms=u, gate=gate)
+    check_walk(s, ids, lp, P, Q, anchor, pidx, score, "sample", temperature, u, gate)
+    # the same uniforms give the same path again
+    _, score2, pidx2 = run_select_opts(s, ids, lp, P, Q, anchor, walk="sample", temperature=temperature,
+                                       uniforms=u, gate=gate)
+    assert np.array_equal(pidx, pidx2) and np.array_equal(score, score2)
+
+
+def test_select_sample_extreme_uniforms():
+    """u = 0 takes the first candidate with a non-zero weight (index 0 when
+    every weight is positive); u just below 1 takes the last."""
+    s = S(batch=2, block=4, vocab=3000, top_k=8, rank=64)
+    ids, lp, P, Q, anchor = select_inputs(s, 95)
+    u0 = np.zeros((s.batch, s.block), np.float32)
+    _, _, p0 = run_select_opts(s, ids, lp, P, Q, anchor, walk="sample", temperature=1e3, uniforms=u0)
+    assert np.all(p0[:, 1:] == 0)
+    u1 = np.full((s.batch, s.block), np.nextafter(np.float32(1), np.float32(0)), np.float32)
+    _, _, p1 = run_select_opts(s, ids, lp, P, Q, anchor, walk="sample", temperature=1e3, uniforms=u1)
+    assert np.all(p1[:, 1:] == s.top_k - 1)
+
+
 # ============================================================== whole block (E2E)
 
 def run_block(s, dev, cfg=None, stream=None):
@@ -399,6 +534,49 @@ def test_draft_block_e2e_small(s):
     dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
     dev["wg_cm"] = to_dev(wg_channel_major(inp["wg"]))
     check_block_e2e(s, inp, dev)
+
+
+@pytest.mark.parametrize("walk", ["viterbi", "greedy", "sample"])
+def test_draft_block_with_options(walk):
+    """The whole block with a context gate and each walk rule, against the
+    oracle's candidates and walk.  Blocks whose GPU candidates differ from the
+    oracle's by a near tie are not walked."""
+    s = S(batch=6, block=8, hidden=256, vocab=6000, top_k=16, rank=64)
+    inp = wl.make_inputs_for(s, 101)
+    dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
+    dev["wg_cm"] = to_dev(wg_channel_major(inp["wg"]))
+    gate = gate_for(s, 102)
+    u = np.random.default_rng(103).random((s.batch, s.block)).astype(np.float32)
+    cfg = dfs.Config.of(s)
+    path = empty((s.batch, s.block), torch.int32)
+    score = empty((s.batch,), torch.float32)
+    ids = empty((s.rows, s.top_k), torch.int32)
+    lp = empty((s.rows, s.top_k), torch.float32)
+    extra = dict(temperature=0.8, uniforms=to_dev(u)) if walk == "sample" else {}
+    dfs.draft_block(cfg, dev["h"], dev["anchor"], dev["wg_cm"], dev["W"], dev["P"], dev["Q"], path, score,
+                    wsbuf(cfg), cand_ids=ids, cand_logp=lp, gate=to_dev(gate), walk=walk, **extra)
+    torch.cuda.synchronize()
+    path, score, ids, lp = from_dev(path), from_dev(score), from_dev(ids), from_dev(lp)
+    ref = orc.draft_block(s, inp["h"], inp["anchor"], inp["wg"], inp["W"], inp["P"], inp["Q"], gate=gate)
+    walked = 0
+    for b in range(s.batch):
+        rs = slice(b * s.block, (b + 1) * s.block)
+        if not np.array_equal(ids[rs], ref["ids"][rs]):
+            continue
+        walked += 1
+        T = orc.transitions(s, int(inp["anchor"][b]), ref["ids"][rs], inp["P"], inp["Q"], gate=gate[rs])
+        if walk == "viterbi":
+            ridx, rsc, margin = orc.viterbi(ref["logp"][rs], T)
+            if margin <= 1e-3:
+                continue
+        else:
+            ridx, rsc = orc.walk(ref["logp"][rs], T, walk, 0.8, u[b].astype(np.float64) if walk == "sample" else None)
+        want = [int(inp["anchor"][b])] + [int(ref["ids"][b * s.block + t, ridx[t]]) for t in range(1, s.block)]
+        if walk == "sample" and list(path[b]) != want:
+            continue  # a uniform on a CDF boundary under the 2e-3 logit tolerance; covered in FED mode
+        assert list(path[b]) == want, (walk, b)
+        assert abs(score[b] - rsc) <= TOL * max(1.0, abs(rsc)), (walk, b)
+    assert walked >= s.batch - 1
 
 
 def test_draft_block_deterministic_and_stream():
