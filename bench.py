@@ -34,6 +34,7 @@ WORKLOAD_NAMES = {
     2: "page drafter shape, batch 1 (B 8, D 5120, V 248320, K 16, r 256, bf16)",
     3: "page drafter shape, batch 32 (B 8, D 5120, V 248320, K 16, r 256, bf16)",
     4: "long block, batch 8 (B 16, D 5120, V 248320, K 16, r 256, bf16)",
+    5: "selector only, conv off: page drafter shape, batch 1 (B 8, D 5120, V 248320, K 16, r 256, bf16, 1 tap)",
 }
 
 
@@ -205,6 +206,20 @@ def main() -> int:
         return a.elapsed_time(b) / n_stage * 1e3  # us
 
     us_conv = timed(lambda: dfs.conv(cfg, h, wg_cm, y, ws, stream=stream))
+    # One conv per drafter layer: five layers in one dfs_conv_layers call
+    # against five dfs_conv calls (inputs: the workload's tensors repeated).
+    NL = 5
+    hL, wgL = h.repeat(NL, 1, 1).contiguous(), wg_cm.repeat(NL, 1, 1).contiguous()
+    yL = torch.empty((NL, s.rows, s.hidden), dtype=tdt, device="cuda")
+    wsL = torch.empty(dfs.conv_layers_workspace_size(cfg, NL), dtype=torch.uint8, device="cuda")
+    us_layers = timed(lambda: dfs.conv_layers(cfg, NL, hL, wgL, yL, wsL, stream=stream))
+
+    def separate():
+        for layer in range(NL):
+            dfs.conv(cfg, hL[layer], wgL[layer], yL[layer], ws, stream=stream)
+
+    us_separate = timed(separate)
+    del hL, wgL, yL, wsL
     us_head = timed(lambda: dfs.head_topk(cfg, y, W, ids, lp, lse, ws, stream=stream))
     us_sel = timed(lambda: dfs.select(cfg, anchor, ids, lp, P, Q, path, score, ws, stream=stream))
 
@@ -249,6 +264,7 @@ def main() -> int:
                    "conv_group_size": s.group, "conv_kernel_size": s.ksize, "parallelism": "none (1 GPU)"},
         "us_per_block": round(ms_step * 1e3 / s.batch, 3),
         "stage_us": {"conv": round(us_conv, 2), "head_topk": round(us_head, 2), "select": round(us_sel, 2)},
+        "conv_layers_us": {"layers": NL, "one_call": round(us_layers, 2), "separate_calls": round(us_separate, 2)},
         "block_hbm_frac": round(block_bytes(s) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "head_mfma_frac": round(head_flops(s) / (us_head * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),

@@ -11,7 +11,11 @@ from .dflash2 import (  # noqa: F401
     Config,
     DFSError,
     STATUS,
+    SelectOpts,
+    WALKS,
     conv,
+    conv_layers,
+    conv_layers_workspace_size,
     draft_block,
     head_topk,
     lib,

@@ -19,6 +19,8 @@ constexpr int kMaxVocab = 1 << 21;        // logits ranked in at most 256 slices
 
 bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
 
+size_t align_up_bytes(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
 int check_cfg(const dfs_config* c) {
     if (!c) return DFS_ERR_NULL;
     if (c->dtype != DFS_F32 && c->dtype != DFS_BF16) return DFS_ERR_UNSUPPORTED;
@@ -87,6 +89,27 @@ int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm, void* y, f
         return DFS_ERR_MISALIGNED;
     if ((st = check_ws(cfg, ws, ws_bytes))) return st;
     return hip_status(dfs::launch_conv(dims_of(cfg), h, wg_cm, y, y_f32, (char*)ws, (hipStream_t)stream));
+}
+
+constexpr int kMaxLayers = 64;
+
+size_t dfs_conv_layers_workspace_size(const dfs_config* cfg, int32_t layers) {
+    if (check_cfg(cfg) != DFS_OK || layers < 1 || layers > kMaxLayers) return 0;
+    const Dims d = dims_of(cfg);
+    return align_up_bytes(dfs::ws_layout(d).zpart + (size_t)layers * dfs::conv_ws_bytes(d), 256);
+}
+
+int dfs_conv_layers(const dfs_config* cfg, int32_t layers, const void* h, const void* wg_cm, void* y, void* ws,
+                    size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (layers < 1 || layers > kMaxLayers) return DFS_ERR_SHAPE;
+    if (!h || !wg_cm || !y || !ws) return DFS_ERR_NULL;
+    if (misaligned(h, 16) || misaligned(wg_cm, 16) || misaligned(y, 16) || misaligned(ws, 256))
+        return DFS_ERR_MISALIGNED;
+    if (ws_bytes < dfs_conv_layers_workspace_size(cfg, layers)) return DFS_ERR_WORKSPACE;
+    return hip_status(
+        dfs::launch_conv(dims_of(cfg), h, wg_cm, y, nullptr, (char*)ws, (hipStream_t)stream, (int)layers));
 }
 
 int dfs_head_topk(const dfs_config* cfg, const void* y, const void* W, int32_t* cand_ids, float* cand_logp,
@@ -162,11 +185,12 @@ int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts, const vo
     const dfs::WsLayout L = dfs::ws_layout(d);
     char* w = (char*)ws;
     hipStream_t s = (hipStream_t)stream;
-    void* y = w + L.y;
+    // One tap: the conv is the identity, so the head reads h directly.
+    const void* y = d.ks == 1 ? h : (const void*)(w + L.y);
     int32_t* cids = cand_ids ? cand_ids : (int32_t*)(w + L.cids);
     float* clogp = cand_logp ? cand_logp : (float*)(w + L.clogp);
     float* lse = (float*)(w + L.lse);
-    if ((st = hip_status(dfs::launch_conv(d, h, wg_cm, y, nullptr, w, s)))) return st;
+    if (d.ks != 1 && (st = hip_status(dfs::launch_conv(d, h, wg_cm, w + L.y, nullptr, w, s)))) return st;
     if ((st = hip_status(dfs::launch_head_topk(d, y, W, cids, clogp, lse, nullptr, w, s)))) return st;
     return hip_status(dfs::launch_select(d, o, anchor, cids, clogp, P, Q, path, path_score, nullptr, w, s));
 }

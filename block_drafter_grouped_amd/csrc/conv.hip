@@ -34,10 +34,15 @@ __global__ __launch_bounds__(kGenWaves * kWave) void conv_gen_kernel(const uint1
                                                                    const uint16_t* __restrict__ wg,
                                                                    float* __restrict__ zpart, int rows, int D,
                                                                    int C) {
+    // grid z = layer * kConvSplit + split; layers are independent [rows, D]
+    // inputs with their own generator.
     __shared__ float red[kGenWaves][NF][4][kWave];
     const int col0 = blockIdx.x * 16;
     const int row0 = blockIdx.y * 16 * NF;
-    const int split = blockIdx.z;
+    const int split = blockIdx.z % kConvSplit, layer = blockIdx.z / kConvSplit;
+    h += (size_t)layer * rows * D;
+    wg += (size_t)layer * C * D;
+    zpart += (size_t)layer * kConvSplit * rows * C;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int i16 = lane & 15, q = lane >> 4;
     const int nf = min(NF, (rows - row0 + 15) / 16);
@@ -104,6 +109,13 @@ __global__ __launch_bounds__(256) void conv_apply_kernel(const uint16_t* __restr
     __shared__ float wt[16][17];
     const int col0 = blockIdx.x * 16, row0 = blockIdx.y * 16;
     const int t0 = threadIdx.x;
+    {  // grid z = layer
+        const size_t l = blockIdx.z;
+        h += l * rows * D;
+        zpart += l * kConvSplit * rows * C;
+        y += l * rows * D;
+        if (y_f32) y_f32 += l * rows * D;
+    }
     {
         const int rr = t0 / 16, cc = t0 % 16, row = row0 + rr, col = col0 + cc;
         float z = 0.f;
@@ -147,6 +159,13 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const float* __restrict__
                                                        int B, int D, int gs, int ks, int C) {
     extern __shared__ float sm[];  // z[C] then w[C]
     const int row = blockIdx.x, t = row % B;
+    {  // grid y = layer
+        const size_t l = blockIdx.y;
+        h += l * rows * D;
+        wg += l * C * D;
+        y += l * rows * D;
+        if (y_f32) y_f32 += l * rows * D;
+    }
     for (int col = threadIdx.x; col < C; col += blockDim.x) {
         float acc = 0.f;
         for (int c = 0; c < D; ++c) acc += h[(size_t)row * D + c] * wg[(size_t)col * D + c];
@@ -178,26 +197,31 @@ size_t conv_ws_bytes(const Dims& d) {
 }
 
 hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32, char* ws,
-                       hipStream_t s) {
+                       hipStream_t s, int layers) {
     const int C = d.taps();
+    if (d.ks == 1 && !y_f32) {
+        // One tap: the tap softmax is 1, so y = h (already in the dtype).
+        return hipMemcpyAsync(y, h, (size_t)layers * d.rows() * d.D * (d.bf16 ? 2 : 4), hipMemcpyDeviceToDevice,
+                              s);
+    }
     if (d.bf16) {
         float* zpart = (float*)(ws + ws_layout(d).zpart);
         if (d.rows() <= 16) {
-            dim3 grid((C + 15) / 16, 1, kConvSplit);
+            dim3 grid((C + 15) / 16, 1, kConvSplit * layers);
             conv_gen_kernel<1, 8><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
                                                                     zpart, d.rows(), d.D, C);
         } else {
-            dim3 grid((C + 15) / 16, (d.rows() + 63) / 64, kConvSplit);
+            dim3 grid((C + 15) / 16, (d.rows() + 63) / 64, kConvSplit * layers);
             conv_gen_kernel<4, 4><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
                                                                     zpart, d.rows(), d.D, C);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        dim3 grid2((C + 15) / 16, (d.rows() + 15) / 16);
+        dim3 grid2((C + 15) / 16, (d.rows() + 15) / 16, layers);
         conv_apply_kernel<<<grid2, 256, 0, s>>>((const uint16_t*)h, zpart, (uint16_t*)y, y_f32, d.rows(), d.B, d.D,
                                                 d.gs, d.ks, C);
     } else {
-        conv_f32_kernel<<<d.rows(), 256, 2 * (size_t)C * sizeof(float), s>>>(
+        conv_f32_kernel<<<dim3(d.rows(), layers), 256, 2 * (size_t)C * sizeof(float), s>>>(
             (const float*)h, (const float*)wg_cm, (float*)y, y_f32, d.rows(), d.B, d.D, d.gs, d.ks, C);
     }
     return hipGetLastError();

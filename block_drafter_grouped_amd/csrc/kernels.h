@@ -30,11 +30,16 @@ struct WsLayout {
 };
 WsLayout ws_layout(const Dims& d);
 
-// Bytes of split-reduction partials the bf16 conv keeps in the workspace.
+// Bytes of split-reduction partials the bf16 conv keeps in the workspace,
+// per layer.  They are the workspace's last section (ws_layout().zpart), so
+// a conv over several layers needs zpart + layers * conv_ws_bytes bytes.
 size_t conv_ws_bytes(const Dims& d);
 
+// The conv of `layers` independent [rows, D] inputs, each with its own
+// generator: h [layers, rows, D], wg_cm [layers, G*ks, D], y and y_f32
+// [layers, rows, D].
 hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32, char* ws,
-                       hipStream_t s);
+                       hipStream_t s, int layers = 1);
 
 // Head + top-K.  Uses ws.keys / ws.ms, and ws.logits when the logits are
 // ranked after the head (fp32, K > 16, more than 8 rows) and logits_f32 is

@@ -27,6 +27,7 @@ STATUS = {
 }
 
 EXPORTS = ("dfs_workspace_size", "dfs_status_string", "dfs_validate_config", "dfs_conv",
+           "dfs_conv_layers", "dfs_conv_layers_workspace_size",
            "dfs_head_topk", "dfs_topk_logits", "dfs_select", "dfs_draft_block")
 
 
@@ -87,6 +88,9 @@ def _load():
     lib_.dfs_status_string.restype = C.c_char_p
     lib_.dfs_validate_config.argtypes = [cfg]
     lib_.dfs_conv.argtypes = [cfg, P, P, P, P, P, S, P]
+    lib_.dfs_conv_layers.argtypes = [cfg, I, P, P, P, P, S, P]
+    lib_.dfs_conv_layers_workspace_size.restype = S
+    lib_.dfs_conv_layers_workspace_size.argtypes = [cfg, I]
     lib_.dfs_head_topk.argtypes = [cfg, P, P, P, P, P, P, P, S, P]
     lib_.dfs_topk_logits.argtypes = [cfg, P, P, P, P, P, S, P]
     lib_.dfs_select.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, S, P]
@@ -141,6 +145,15 @@ def validate_config(cfg: Config) -> int:
 def conv(cfg, h, wg_cm, y, ws, y_f32=None, stream=None):
     _check(_lib.dfs_conv(C.byref(cfg), _ptr(h), _ptr(wg_cm), _ptr(y), _ptr(y_f32), _ptr(ws), _nbytes(ws),
                          _stream(stream)), "dfs_conv")
+
+
+def conv_layers_workspace_size(cfg: Config, layers: int) -> int:
+    return _lib.dfs_conv_layers_workspace_size(C.byref(cfg), layers)
+
+
+def conv_layers(cfg, layers, h, wg_cm, y, ws, stream=None):
+    _check(_lib.dfs_conv_layers(C.byref(cfg), layers, _ptr(h), _ptr(wg_cm), _ptr(y), _ptr(ws), _nbytes(ws),
+                                _stream(stream)), "dfs_conv_layers")
 
 
 def head_topk(cfg, y, W, cand_ids, cand_logp, lse, ws, logits_f32=None, stream=None):

@@ -119,6 +119,27 @@ int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm,
              void* y, float* y_f32, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Step 1 for several drafter layers in one pair of launches (release-note
+ * article, cost section: the conv ran as 20 small calls per step for a
+ * 5-layer drafter, which reads as one conv per layer).  Layer l applies
+ * dfs_conv's operation to its own hidden states with its own generator:
+ *
+ *  layers          1..64 (else DFS_ERR_SHAPE)
+ *  h      [layers, rows, D]   dtype
+ *  wg_cm  [layers, G*ks, D]   dtype, channel-major as for dfs_conv
+ *  y      [layers, rows, D]   dtype out
+ *  ws, ws_bytes  at least dfs_conv_layers_workspace_size(cfg, layers) bytes,
+ *                256-B aligned
+ * Layer results equal dfs_conv on each layer alone.
+ */
+int dfs_conv_layers(const dfs_config* cfg, int32_t layers, const void* h,
+                    const void* wg_cm, void* y, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Workspace bytes dfs_conv_layers needs (0 if cfg or layers is invalid). */
+size_t dfs_conv_layers_workspace_size(const dfs_config* cfg, int32_t layers);
+
+/*
  * Steps 2-3: vocabulary head, log-softmax and per-slot top-K for every row.
  *
  *   logit[row, v] = sum_c y[row, c] * W[v, c]           (fp32 accumulation)

@@ -48,7 +48,7 @@ def cfg_of(cfg_id=2, **kw):
     return c
 
 
-@pytest.mark.parametrize("cfg_id", range(5))
+@pytest.mark.parametrize("cfg_id", sorted(wl.CONFIGS))
 def test_workload_configs_are_valid(cfg_id):
     c = cfg_of(cfg_id)
     assert dfs.validate_config(c) == OK
@@ -116,6 +116,21 @@ def test_conv_validation():
     assert call("dfs_conv", *conv_args(c, nbytes=dfs.workspace_size(c) - 1)) == WS
     assert call("dfs_conv", *conv_args(c, ws=None)) == NULL
     assert call("dfs_conv", *conv_args(c, ws=A + 16)) == MISAL
+
+
+def test_conv_layers_validation():
+    c = cfg_of(2)
+    n = dfs.conv_layers_workspace_size(c, 5)
+    assert n > dfs.conv_layers_workspace_size(c, 1) > 0
+    assert dfs.conv_layers_workspace_size(c, 0) == 0 and dfs.conv_layers_workspace_size(c, 65) == 0
+    assert dfs.conv_layers_workspace_size(cfg_of(2, block_size=1), 5) == 0
+    assert L.dfs_conv_layers(C.byref(c), 0, A, A, A, A, n, None) == SHAPE
+    assert L.dfs_conv_layers(C.byref(c), 65, A, A, A, A, n, None) == SHAPE
+    assert L.dfs_conv_layers(C.byref(c), 5, None, A, A, A, n, None) == NULL
+    assert L.dfs_conv_layers(C.byref(c), 5, A, A, A, None, n, None) == NULL
+    assert L.dfs_conv_layers(C.byref(c), 5, A, A + 8, A, A, n, None) == MISAL
+    assert L.dfs_conv_layers(C.byref(c), 5, A, A, A, A + 16, n, None) == MISAL
+    assert L.dfs_conv_layers(C.byref(c), 5, A, A, A, A, n - 1, None) == WS
 
 
 def test_head_topk_validation():

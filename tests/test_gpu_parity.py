@@ -65,6 +65,7 @@ CONV_SHAPES = [
     S(batch=13, block=8, hidden=512),
     S(batch=2, block=6, hidden=128, ksize=4, dtype="f32"),
     S(batch=3, block=16, hidden=64, group=64, ksize=2),
+    S(batch=2, block=5, hidden=96, ksize=1, dtype="f32"),
 ]
 
 
@@ -96,6 +97,37 @@ def test_conv_parity(s):
     dfs.conv(cfg, h, wg, y2, ws)
     torch.cuda.synchronize()
     assert np.array_equal(from_dev(y2), y_h)
+
+
+@pytest.mark.parametrize("s", [
+    S(batch=1, block=8, hidden=256),                       # <= 16 rows
+    S(batch=5, block=8, hidden=128, group=8, ksize=4),     # > 16 rows
+    S(batch=2, block=8, hidden=128, ksize=1),              # one tap
+    S(batch=2, block=6, hidden=96, ksize=2, dtype="f32"),
+], ids=str)
+def test_conv_layers_parity(s):
+    """dfs_conv_layers: each layer equals dfs_conv on that layer alone (same
+    kernels, bit for bit), whose fp32 result matches the oracle conv of that
+    layer."""
+    L = 3
+    layers = [wl.make_inputs_for(s, 200 + l, parts=("h", "wg")) for l in range(L)]
+    cfg = dfs.Config.of(s)
+    h = to_dev(np.stack([x["h"] for x in layers]))
+    wg = to_dev(np.stack([wg_channel_major(x["wg"]) for x in layers]))
+    y = empty((L, s.rows, s.hidden), tdtype(s))
+    ws = empty((dfs.conv_layers_workspace_size(cfg, L),), torch.uint8)
+    dfs.conv_layers(cfg, L, h, wg, y, ws)
+    torch.cuda.synchronize()
+    got = from_dev(y)
+    for l, x in enumerate(layers):
+        y1 = empty((s.rows, s.hidden), tdtype(s))
+        yf1 = empty((s.rows, s.hidden), torch.float32)
+        dfs.conv(cfg, to_dev(x["h"]), to_dev(wg_channel_major(x["wg"])), y1, wsbuf(cfg), y_f32=yf1)
+        torch.cuda.synchronize()
+        assert np.array_equal(got[l], from_dev(y1)), l
+        # the fp32 result before rounding against the exact conv of the layer
+        _, _, yhat = orc.conv(s, x["h"], x["wg"])
+        assert rel_err(from_dev(yf1), yhat) <= TOL, l
 
 
 # ============================================================== head + top-K (FED)
@@ -511,7 +543,7 @@ def check_block_e2e(s, inp, dev, blocks=None):
     return path, score
 
 
-@pytest.mark.parametrize("cfg_id", [0, 1, 2])
+@pytest.mark.parametrize("cfg_id", [0, 1, 2, 5])
 def test_draft_block_e2e(cfg_id):
     s = wl.shape_of(cfg_id)
     inp, dev = cfg_inputs(cfg_id)
@@ -528,6 +560,7 @@ def test_draft_block_e2e_batch32_sampled():
     S(batch=4, block=5, hidden=128, vocab=7000, top_k=8, rank=32),
     S(batch=3, block=16, hidden=64, vocab=1000, top_k=16, rank=16, ksize=4, group=32),
     S(batch=2, block=8, hidden=96, vocab=800, top_k=20, rank=24, dtype="f32"),
+    S(batch=3, block=6, hidden=128, vocab=4000, top_k=16, rank=32, ksize=1),
 ], ids=str)
 def test_draft_block_e2e_small(s):
     inp = wl.make_inputs_for(s, 17)

@@ -61,6 +61,9 @@ CONFIGS = {
     2: Shape(batch=1, block=8, hidden=5120, vocab=248320, top_k=16, rank=256, group=16, ksize=2, dtype="bf16"),
     3: Shape(batch=32, block=8, hidden=5120, vocab=248320, top_k=16, rank=256, group=16, ksize=2, dtype="bf16"),
     4: Shape(batch=8, block=16, hidden=5120, vocab=248320, top_k=16, rank=256, group=16, ksize=2, dtype="bf16"),
+    # selector only: the page shape at batch 1 with the conv off (one tap,
+    # so y = h), as the Inco AI post's Table 2 measures path selection
+    5: Shape(batch=1, block=8, hidden=5120, vocab=248320, top_k=16, rank=256, group=16, ksize=1, dtype="bf16"),
 }
 
 
