@@ -81,7 +81,7 @@ __device__ __forceinline__ void wait_vm(int n) {
     }
 }
 
-template <int NWB, int KC, int RW, int RY>
+template <int NWB, int KC, int RW, int RY, int NVB>
 __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kernel(
     const uint16_t* __restrict__ y, int rows_total, int D, const uint16_t* __restrict__ W, int V, int nch,
     float* __restrict__ logits) {
@@ -151,17 +151,21 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
         return;
     }
 
-    // Consumers.
+    // Consumers.  Wave w computes NVB vocabulary blocks x NRB row blocks of
+    // 32x32 (NVB * NRB = 8): vocabulary blocks NVB * (w % (8 / NVB)) .., row
+    // blocks NRB * (w / (8 / NVB)) ..  Per 16 channels a wave reads NVB + NRB
+    // operand fragments from LDS for 8 MFMAs.
+    constexpr int NRB = 8 / NVB, NVW = 8 / NVB;
     const int j = lane & 31, half = lane >> 5;
-    const int rl = wave * 32 + j;
-    const int my_row = row_base + rl;
-    const bool row_ok = my_row < rows_total;
+    const int vw = wave % NVW, rw = wave / NVW;
     const bool vec4 = (V & 3) == 0;  // rows of the logits are 16-B aligned
-    f32x16 acc[8];
+    f32x16 acc[NVB][NRB];
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb)
+    for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[vb][r] = 0.f;
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[vb][rb][r] = 0.f;
     int tile = 0, st = 0;
     for (int g = 0; g < total; ++g) {
         __syncthreads();  // stage g published
@@ -170,41 +174,53 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
 #pragma unroll
         for (int ks = 0; ks < KC / 16; ++ks) {
             const int u = 2 * ks + half;
-            const bf16x8 b = __builtin_bit_cast(bf16x8, sy[gemm_unit<KC>(rl, u)]);
+            bf16x8 bo[NRB];
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+                bo[rb] = __builtin_bit_cast(bf16x8, sy[gemm_unit<KC>((rw * NRB + rb) * 32 + j, u)]);
             // Rows past the range hold copies of its last row; their results
             // are dropped below.
 #pragma unroll
-            for (int vb = 0; vb < 8; ++vb) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit<KC>(vb * 32 + j, u)]);
-                acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[vb], 0, 0, 0);
+            for (int vb = 0; vb < NVB; ++vb) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit<KC>((vw * NVB + vb) * 32 + j, u)]);
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)
+                    acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bo[rb], acc[vb][rb], 0, 0, 0);
             }
         }
         if (st == S - 1) {
-            // Tile done.  Lane holds, for vocabulary block vb, logit[v][my_row]
-            // in acc[vb][r] with v = base + 32 vb + 8 (r / 4) + 4 half + r % 4.
+            // Tile done.  For vocabulary block vb and row block rb the lane
+            // holds logit[v][row] in acc[vb][rb][r], with row = its row
+            // block's row j and v = base + 32 vb' + 8 (r / 4) + 4 half + r % 4.
             const int vt = v_beg + tile * kGemmTV;
-            if (row_ok) {
-                float* out = logits + (size_t)my_row * V;
 #pragma unroll
-                for (int vb = 0; vb < 8; ++vb) {
+            for (int rb = 0; rb < NRB; ++rb) {
+                const int row = row_base + (rw * NRB + rb) * 32 + j;
+                if (row < rows_total) {
+                    float* out = logits + (size_t)row * V;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int v = vt + 32 * vb + 8 * q + 4 * half;
-                        if (vec4 && v + 3 < v_end) {
-                            *(f32x4*)(out + v) = f32x4{acc[vb][4 * q], acc[vb][4 * q + 1], acc[vb][4 * q + 2],
-                                                       acc[vb][4 * q + 3]};
-                        } else {
+                    for (int vb = 0; vb < NVB; ++vb) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (v + e < v_end) out[v + e] = acc[vb][4 * q + e];
+                        for (int q = 0; q < 4; ++q) {
+                            const int v = vt + 32 * (vw * NVB + vb) + 8 * q + 4 * half;
+                            if (vec4 && v + 3 < v_end) {
+                                *(f32x4*)(out + v) = f32x4{acc[vb][rb][4 * q], acc[vb][rb][4 * q + 1],
+                                                           acc[vb][rb][4 * q + 2], acc[vb][rb][4 * q + 3]};
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (v + e < v_end) out[v + e] = acc[vb][rb][4 * q + e];
+                            }
                         }
                     }
                 }
             }
 #pragma unroll
-            for (int vb = 0; vb < 8; ++vb)
+            for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[vb][r] = 0.f;
+                for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[vb][rb][r] = 0.f;
             ++tile;
             st = 0;
         } else {
@@ -244,12 +260,12 @@ __global__ __launch_bounds__(256) void head_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-template <int NWB, int KC, int RW, int RY>
+template <int NWB, int KC, int RW, int RY, int NVB>
 hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int nch, float* logits, hipStream_t s) {
     constexpr int RP = 32 * NWB;
     constexpr size_t lds = ((size_t)RW * kGemmTV + (size_t)RY * RP) * KC * 2;
     static_assert(lds <= 160 * 1024, "the stage rings must fit in LDS");
-    auto fn = head_gemm_kernel<NWB, KC, RW, RY>;
+    auto fn = head_gemm_kernel<NWB, KC, RW, RY, NVB>;
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid(nch, (d.rows() + RP - 1) / RP);
@@ -258,6 +274,8 @@ hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int n
     return hipGetLastError();
 }
 
+constexpr int kGemmNVB = 4;  // vocabulary blocks per consumer wave (x 2 row blocks)
+
 // More than 8 rows: one pass of the GEMM head per 256 rows instead of one
 // weight stream per 8 rows.
 bool use_gemm_head(const Dims& d) { return d.bf16 && d.rows() > kRowsPass; }
@@ -265,10 +283,10 @@ bool use_gemm_head(const Dims& d) { return d.bf16 && d.rows() > kRowsPass; }
 hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {
     const int nch = head_chunks(d);
     if (d.D % 64 == 0)
-        return d.rows() <= 128 ? launch_head_gemm_t<4, 64, 3, 2>(d, y, W, nch, logits, s)
-                               : launch_head_gemm_t<8, 64, 3, 2>(d, y, W, nch, logits, s);
-    return d.rows() <= 128 ? launch_head_gemm_t<4, 32, 6, 4>(d, y, W, nch, logits, s)
-                           : launch_head_gemm_t<8, 32, 6, 4>(d, y, W, nch, logits, s);
+        return d.rows() <= 128 ? launch_head_gemm_t<4, 64, 3, 2, kGemmNVB>(d, y, W, nch, logits, s)
+                               : launch_head_gemm_t<8, 64, 3, 2, kGemmNVB>(d, y, W, nch, logits, s);
+    return d.rows() <= 128 ? launch_head_gemm_t<4, 32, 6, 4, kGemmNVB>(d, y, W, nch, logits, s)
+                           : launch_head_gemm_t<8, 32, 6, 4, kGemmNVB>(d, y, W, nch, logits, s);
 }
 
 hipError_t launch_head_f32(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {
