@@ -113,7 +113,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(wl.CONFIGS))
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(wl.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline (0: skip)")
     ap.add_argument("--stage-steps", type=int, default=None, help="calls per stage timing loop")
     ap.add_argument("--copy-probe", action="store_true",

@@ -65,7 +65,7 @@ const char* dfs_status_string(int status) {
         case DFS_OK: return "ok";
         case DFS_ERR_NULL: return "a required pointer is NULL";
         case DFS_ERR_SHAPE: return "a size is out of range or inconsistent";
-        case DFS_ERR_UNSUPPORTED: return "value not supported by this build";
+        case DFS_ERR_UNSUPPORTED: return "valid value the library does not implement";
         case DFS_ERR_MISALIGNED: return "tensor not 16-byte aligned (workspace: 256-byte)";
         case DFS_ERR_WORKSPACE: return "workspace smaller than dfs_workspace_size()";
         case DFS_ERR_HIP: return "HIP kernel launch failed";

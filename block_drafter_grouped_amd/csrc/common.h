@@ -22,10 +22,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-template <typename T> __device__ __forceinline__ float to_f32(T x);
-template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
-template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
-
 // ---------------------------------------------------------------------------
 // Candidate keys.  A 64-bit key orders candidates exactly as the method
 // does: larger logit first, equal logits by smaller vocabulary id.  High word:

@@ -62,7 +62,7 @@ typedef enum {
     DFS_OK = 0,
     DFS_ERR_NULL = 1,        /* a required pointer is NULL                    */
     DFS_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
-    DFS_ERR_UNSUPPORTED = 3, /* a valid value this build does not implement    */
+    DFS_ERR_UNSUPPORTED = 3, /* a valid value the library does not implement */
     DFS_ERR_MISALIGNED = 4,  /* a tensor is not 16-B (workspace: 256-B) aligned */
     DFS_ERR_WORKSPACE = 5,   /* ws_bytes < dfs_workspace_size(cfg)             */
     DFS_ERR_HIP = 6          /* a kernel launch failed                         */

@@ -48,7 +48,7 @@ def cfg_of(cfg_id=2, **kw):
     return c
 
 
-@pytest.mark.parametrize("cfg_id", sorted(wl.CONFIGS))
+@pytest.mark.parametrize("cfg_id", sorted(wl.WORKLOADS))
 def test_workload_configs_are_valid(cfg_id):
     c = cfg_of(cfg_id)
     assert dfs.validate_config(c) == OK

@@ -58,8 +58,8 @@ def tdtype(s):
 # ============================================================== conv
 
 CONV_SHAPES = [
-    wl.CONFIGS[0],
-    wl.CONFIGS[0].with_(dtype="bf16"),
+    wl.WORKLOADS[0],
+    wl.WORKLOADS[0].with_(dtype="bf16"),
     S(batch=3, block=5, hidden=96, group=8, ksize=4),
     S(batch=2, block=7, hidden=256, group=32, ksize=1),
     S(batch=13, block=8, hidden=512),
@@ -133,7 +133,7 @@ def test_conv_layers_parity(s):
 # ============================================================== head + top-K (FED)
 
 HEAD_SHAPES = [
-    wl.CONFIGS[0],
+    wl.WORKLOADS[0],
     S(block=8, hidden=64, vocab=1000, top_k=4),
     S(block=3, hidden=128, vocab=4097, top_k=16),
     S(batch=5, block=4, hidden=256, vocab=20000, top_k=16),

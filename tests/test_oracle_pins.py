@@ -453,12 +453,12 @@ def _numpy_pipeline_paths(s, inp, orc):
 
 
 @pytest.mark.parametrize("shape", [
-    wl.CONFIGS[0],
-    wl.CONFIGS[0].with_(batch=3, block=5, vocab=777, top_k=3, dtype="bf16"),
-    wl.CONFIGS[0].with_(batch=2, block=3, hidden=96, group=8, ksize=4, vocab=513, top_k=5),
+    wl.WORKLOADS[0],
+    wl.WORKLOADS[0].with_(batch=3, block=5, vocab=777, top_k=3, dtype="bf16"),
+    wl.WORKLOADS[0].with_(batch=2, block=3, hidden=96, group=8, ksize=4, vocab=513, top_k=5),
 ])
 def test_draft_block_matches_independent_pipeline(orc, shape):
-    inp = wl.make_inputs_for(shape, 0 if shape == wl.CONFIGS[0] else 55)
+    inp = wl.make_inputs_for(shape, 0 if shape == wl.WORKLOADS[0] else 55)
     out = orc.draft_block(shape, inp["h"], inp["anchor"], inp["wg"], inp["W"], inp["P"], inp["Q"])
     ids, logp, lse, paths, scores = _numpy_pipeline_paths(shape, inp, orc)
     assert np.array_equal(out["ids"], ids)
@@ -469,7 +469,7 @@ def test_draft_block_matches_independent_pipeline(orc, shape):
 
 
 def test_draft_block_zero_selector_is_dflash1_argmax(orc):
-    s = wl.CONFIGS[0].with_(batch=2)
+    s = wl.WORKLOADS[0].with_(batch=2)
     inp = wl.make_inputs_for(s, 61)
     zero = np.zeros_like(inp["P"])
     out = orc.draft_block(s, inp["h"], inp["anchor"], inp["wg"], inp["W"], zero, inp["Q"])
@@ -480,7 +480,7 @@ def test_draft_block_zero_selector_is_dflash1_argmax(orc):
 
 
 def test_draft_block_bad_anchor(orc):
-    s = wl.CONFIGS[0].with_(batch=3)
+    s = wl.WORKLOADS[0].with_(batch=3)
     inp = wl.make_inputs_for(s, 62)
     anchor = inp["anchor"].copy()
     anchor[1] = s.vocab

@@ -5,7 +5,7 @@ none of the method's arithmetic: only random draws, scaling of those draws to
 the stated standard deviations, and the fp32 -> bf16 storage conversion.
 """
 from .synth import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     TENSOR_IDS,
     Shape,
     shape_of,

@@ -55,7 +55,7 @@ class Shape:
         return replace(self, **kw)
 
 
-CONFIGS = {
+WORKLOADS = {
     0: Shape(batch=1, block=4, hidden=64, vocab=1000, top_k=4, rank=16, group=16, ksize=2, dtype="f32"),
     1: Shape(batch=1, block=8, hidden=2560, vocab=151936, top_k=16, rank=256, group=16, ksize=2, dtype="bf16"),
     2: Shape(batch=1, block=8, hidden=5120, vocab=248320, top_k=16, rank=256, group=16, ksize=2, dtype="bf16"),
@@ -68,7 +68,7 @@ CONFIGS = {
 
 
 def shape_of(cfg: int) -> Shape:
-    return CONFIGS[cfg]
+    return WORKLOADS[cfg]
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -171,4 +171,4 @@ def make_inputs(cfg: int, parts=("h", "wg", "W", "P", "Q", "anchor")) -> dict:
     Workload 4 additionally plants transition bonuses; that step needs the
     oracle's candidates and lives with the tests, not here.
     """
-    return make_inputs_for(CONFIGS[cfg], cfg, parts)
+    return make_inputs_for(WORKLOADS[cfg], cfg, parts)
