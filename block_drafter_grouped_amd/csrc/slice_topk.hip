@@ -105,10 +105,11 @@ __global__ __launch_bounds__(kSliceThreads, 4) void slice_topk_kernel(const floa
         theta_sh = 0ull;
     }
     __syncthreads();
-    if (t < 64) {
-        const uint64_t g = gmax[t];
+    if (wave == 0) {  // lane i ranks group maximum i against the other 63 (register broadcasts)
+        const uint64_t g = gmax[lane];
         int rank = 0;
-        for (int i = 0; i < 64; ++i) rank += gmax[i] > g ? 1 : 0;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) rank += readlane_u64(g, i) > g ? 1 : 0;
         if (rank == K - 1 && g != 0ull) theta_sh = g;  // fewer than K non-empty groups: theta stays 0
         if (rank == 0) top_sh = g;                      // unique when g != 0; all-empty slices write 0
     }

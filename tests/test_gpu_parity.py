@@ -204,6 +204,34 @@ def test_head_topk_fed_full_size(cfg_id):
     check_head_fed(s, inp["h"], inp["W"], W_dev=dev["W"])
 
 
+@pytest.mark.parametrize("s", [
+    S(block=8, hidden=256, vocab=5000, top_k=16),              # streaming head
+    S(batch=2, block=8, hidden=256, vocab=5000, top_k=16),     # GEMM head + slice top-K
+    S(block=8, hidden=256, vocab=3000, top_k=40),              # K > 16
+], ids=str)
+@pytest.mark.parametrize("kind", ["zero_rows", "duplicate_weights"])
+def test_head_topk_massive_ties(s, kind):
+    """Degenerate heads: all hidden rows zero (every logit 0: the candidates
+    are ids 0..K-1 and lse = log V), or weight rows repeating with period 13
+    (every logit value repeats, so ties are broken by id alone).  Exercises
+    the tie fallbacks of the merge and the slice top-K."""
+    inp = wl.make_inputs_for(s, 111, parts=("h", "W"))
+    y, W = inp["h"].copy(), inp["W"].copy()
+    if kind == "zero_rows":
+        y[:] = 0
+    else:
+        W[:] = W[np.arange(s.vocab) % 13]
+    ids, lp, lse, logits = run_head(s, y, W)
+    rid, rlse = topk_of(logits, s.top_k)
+    assert np.array_equal(ids, rid)
+    ref = orc.head(s, y, W, want_logits=True)
+    assert np.array_equal(ids, ref["ids"])
+    assert rel_err(lse, ref["lse"]) <= 1e-5
+    if kind == "zero_rows":
+        assert np.all(ids == np.arange(s.top_k)[None, :])
+        assert np.allclose(lse, np.log(s.vocab), rtol=1e-6)
+
+
 # ============================================================== top-K of given logits
 
 def crafted_logits(rows, V, seed):
