@@ -52,15 +52,27 @@ __device__ __forceinline__ int gemm_unit(int row, int u) {
     return row * (KC / 8) + (u ^ gemm_swz<KC>(row));
 }
 
-// 16-B global -> LDS copy per lane; lane L writes lds_base + 16 L.
+// 16-B global -> LDS copy per lane; lane L writes lds_base + 16 L.  STREAM
+// marks data read once (the weight): a non-temporal load, so that it does
+// not push the reused hidden rows out of L2.
+template <bool STREAM>
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
-                 "v"(g)
-                 : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(
+                         __builtin_amdgcn_readfirstlane(lds_base)),
+                     "v"(g)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(
+                         __builtin_amdgcn_readfirstlane(lds_base)),
+                     "v"(g)
+                     : "memory", "m0");
 #pragma clang diagnostic pop
 }
+
+constexpr bool kGemmStreamW = true;
 
 constexpr int kGemmProducers = 4;  // two W loaders, two hidden-row loaders
 
@@ -124,7 +136,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
                 const int vr = RPI * n + lane / UPR;
                 const int u = (lane % UPR) ^ gemm_swz<KC>(vr);
                 const int v = min(v0 + vr, v_end - 1);  // past the range: re-read its last row (cache hit)
-                dma16(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
+                dma16<kGemmStreamW>(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
             }
         };
         auto issue_y = [&](int g) {
@@ -136,7 +148,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
                 const int r = RPI * n + lane / UPR;
                 const int u = (lane % UPR) ^ gemm_swz<KC>(r);
                 const int row = min(row_base + r, rows_total - 1);
-                dma16(y + (size_t)row * D + k0 + 8 * u, base + n * 1024);
+                dma16<false>(y + (size_t)row * D + k0 + 8 * u, base + n * 1024);
             }
         };
         const int R = wl ? RW : RY, per = wl ? WI : YI;
