@@ -24,7 +24,7 @@ namespace {
 // over kConvSplit workgroups per tile, whose partial tiles go to the
 // workspace; a second kernel sums them in a fixed order, applies the tap
 // softmax and the causal taps.
-constexpr int kConvSplit = 8;
+constexpr int kConvSplit = 4;
 constexpr int kGenWaves = 4;
 
 // NF MFMA row fragments (16 rows each) per workgroup.  Each wave puts the
