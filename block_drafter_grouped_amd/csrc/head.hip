@@ -7,16 +7,18 @@
 // head that writes the logits (gemm_head.hip) is followed by the slice top-K
 // (slice_topk.hip).  A merge kernel here combines the chunk partials.
 //
-// bf16 head (rows <= 8 per pass): the work is a stream of the [V, D] weight
-// (2.5 GB at D 5120, V 248 320) against a tiny [rows, D] operand, so it is
-// bound by HBM.  One persistent workgroup per CU owns a contiguous range of
-// 16-row vocabulary tiles; the hidden rows sit in LDS for the whole kernel,
+// bf16 streaming head (up to 8 rows): the work is a stream of the [V, D]
+// weight (2.5 GB at D 5120, V 248 320) against a tiny [rows, D] operand, so
+// it is bound by HBM.  One persistent workgroup per CU owns a contiguous
+// range of vocabulary tiles; the hidden rows sit in LDS for the whole kernel,
 // pre-swizzled into MFMA B-operand order, and every wave streams its tiles
-// with v_mfma_f32_16x16x32_bf16 while U k-steps of weight loads (1 KB each)
-// are in flight.  The MFMA's 16 output columns hold the (<= 8) rows, so half
-// of each MFMA is padding -- harmless, the kernel waits on HBM.  Each lane
-// then owns 4 consecutive vocabulary entries of one row per tile and keeps a
-// sorted register list of its best keys plus an online (max, sum of exp).
+// with v_mfma_f32_16x16x32_bf16 while U k-steps of weight loads are in
+// flight.  The MFMA's 16 output columns hold the (<= 8) rows, so part of each
+// MFMA is padding -- harmless, the kernel waits on HBM.  The lanes that own
+// results keep a sorted register list of their best keys plus an online
+// (max, sum of exp).  head_pair_kernel (below) serves D % 64 == 0, the page
+// shapes; head_bf16_kernel, with 16-row tiles of 64-B row pieces, serves the
+// other D.
 #include <algorithm>
 
 #include "common.h"
@@ -289,11 +291,11 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
 
 // Chunk partials -> candidates.  Partial keys are stored element-major,
 // [row][k][chunk], so that threads reading consecutive chunks coalesce.
-//  K <= 64: one workgroup (4 waves) per row: a K-round tournament per wave
-//    over its 64 chunk lists, then over the 4 wave lists.
 // lse = M + log S with (M, S) the combined (max, sum of exp), combined in a
 // fixed order.
-// K <= 16, nch <= 256: one workgroup of 1024 threads per row.  Thread t owns
+// K > 16 (merge64_kernel): one workgroup (4 waves) per row: a K-round
+// tournament per wave over its 64 chunk lists, then over the 4 wave lists.
+// K <= 16, nch <= 256 (merge16_kernel): one workgroup of 1024 threads per row.  Thread t owns
 // keys 4*(t/256) .. +3 of chunk t%256 (coalesced loads).  The threshold
 // theta is the minimum over 16 groups of the group's largest key, the
 // groups being 16 consecutive keys of the first 256 partial keys in

@@ -4,16 +4,19 @@
 // of candidates is scored at once with per-token rank-r embeddings, and the
 // only sequential work is the walk over those precomputed scores; the walk
 // starts from the last verified token, as in the vLLM release-note article,
-// section "two additions").  The context gate of the post is taken as 1.
+// section "two additions").  The post's context gate H(h_t) is optional: the
+// caller supplies it, or it is 1.
 //
 // Fast path (bf16 tables, K <= 16, no gate, best-path walk): select_fused_kernel,
 // below.  General path:
 // sel_dots: one workgroup per (draft slot, block) computes the K x K matrix
-//   T_t[j, k] = <P[c_{t-1, j}], Q[c_{t, k}]>   (c_0 = {anchor}: a 1 x K row)
-// from rows gathered out of P and Q, fp32 accumulation.
+//   T_t[j, k] = sum_i P[c_{t-1, j}, i] * H_t[i] * Q[c_{t, k}, i]
+// (c_0 = {anchor}: a 1 x K row) from rows gathered out of P and Q, fp32
+// accumulation.
 // viterbi: one wavefront per block, lane k = candidate k.  The max over
 // predecessors broadcasts delta_{t-1}[j] with v_readlane; the final argmax
-// uses a butterfly max and a ballot (lowest lane wins ties).
+// uses a DPP max and a ballot (lowest lane wins ties).
+// walk: the greedy and sampled walks, one wavefront per block.
 #include "common.h"
 #include "kernels.h"
 

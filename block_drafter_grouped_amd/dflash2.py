@@ -152,6 +152,8 @@ def conv_layers_workspace_size(cfg: Config, layers: int) -> int:
 
 
 def conv_layers(cfg, layers, h, wg_cm, y, ws, stream=None):
+    """dfs_conv_layers: h [layers, rows, D], wg_cm [layers, G*ks, D] -> y
+    [layers, rows, D]; ws of conv_layers_workspace_size(cfg, layers) bytes."""
     _check(_lib.dfs_conv_layers(C.byref(cfg), layers, _ptr(h), _ptr(wg_cm), _ptr(y), _ptr(ws), _nbytes(ws),
                                 _stream(stream)), "dfs_conv_layers")
 
@@ -168,6 +170,8 @@ def topk_logits(cfg, logits, cand_ids, cand_logp, lse, ws, stream=None):
 
 def select(cfg, anchor, cand_ids, cand_logp, P, Q, path, path_score, ws, path_idx=None, stream=None,
            gate=None, walk="viterbi", temperature=1.0, uniforms=None):
+    """dfs_select.  gate: fp32 [rows, r] context gate or None; walk: "viterbi",
+    "greedy" or "sample" (then temperature > 0 and fp32 uniforms [batch, B])."""
     _check(_lib.dfs_select(C.byref(cfg), _opts(gate, walk, temperature, uniforms), _ptr(anchor), _ptr(cand_ids),
                            _ptr(cand_logp), _ptr(P), _ptr(Q), _ptr(path), _ptr(path_score), _ptr(path_idx),
                            _ptr(ws), _nbytes(ws), _stream(stream)), "dfs_select")
@@ -175,6 +179,8 @@ def select(cfg, anchor, cand_ids, cand_logp, P, Q, path, path_score, ws, path_id
 
 def draft_block(cfg, h, anchor, wg_cm, W, P, Q, path, path_score, ws, cand_ids=None, cand_logp=None,
                 stream=None, gate=None, walk="viterbi", temperature=1.0, uniforms=None):
+    """dfs_draft_block: conv, head + top-K and selector on one stream; the
+    selector options as for select()."""
     _check(_lib.dfs_draft_block(C.byref(cfg), _opts(gate, walk, temperature, uniforms), _ptr(h), _ptr(anchor),
                                 _ptr(wg_cm), _ptr(W), _ptr(P), _ptr(Q), _ptr(path), _ptr(path_score),
                                 _ptr(cand_ids), _ptr(cand_logp), _ptr(ws), _nbytes(ws), _stream(stream)),
