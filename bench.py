@@ -222,6 +222,14 @@ def main() -> int:
     del hL, wgL, yL, wsL
     us_head = timed(lambda: dfs.head_topk(cfg, y, W, ids, lp, lse, ws, stream=stream))
     us_sel = timed(lambda: dfs.select(cfg, anchor, ids, lp, P, Q, path, score, ws, stream=stream))
+    # One GPU's share under vocabulary sharding over 8 GPUs: the head + top-K
+    # stage on an eighth of the weight (the merge of the shards' partials is
+    # a few KB per row, left out).
+    vs = s.vocab // 8
+    cfg8 = dfs.Config.of(s.with_(vocab=vs))
+    ws8 = torch.empty(dfs.workspace_size(cfg8), dtype=torch.uint8, device="cuda")
+    us_shard = timed(lambda: dfs.head_topk(cfg8, y, W[:vs], ids, lp, lse, ws8, stream=stream))
+    del ws8
 
     hb = head_stage_bytes(s)
     traffic = recorded_traffic(args.workload)
@@ -265,6 +273,9 @@ def main() -> int:
         "us_per_block": round(ms_step * 1e3 / s.batch, 3),
         "stage_us": {"conv": round(us_conv, 2), "head_topk": round(us_head, 2), "select": round(us_sel, 2)},
         "conv_layers_us": {"layers": NL, "one_call": round(us_layers, 2), "separate_calls": round(us_separate, 2)},
+        "vocab_shard_of_8": {"vocab": vs, "head_topk_us": round(us_shard, 2),
+                             "GBps": round((vs * s.hidden + s.rows * s.hidden) * (2 if s.dtype == "bf16" else 4)
+                                           / (us_shard * 1e-6) / 1e9, 1)},
         "block_hbm_frac": round(block_bytes(s) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "head_mfma_frac": round(head_flops(s) / (us_head * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),

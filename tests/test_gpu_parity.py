@@ -232,6 +232,45 @@ def test_head_topk_massive_ties(s, kind):
         assert np.allclose(lse, np.log(s.vocab), rtol=1e-6)
 
 
+@pytest.mark.parametrize("cfg_id", [1, 3])
+def test_vocab_sharding_merge(cfg_id):
+    """The multi-GPU reading: each GPU runs the head on its eighth of the
+    vocabulary; exchanging the per-row top-K (with global ids) and lse, then
+    merging, must give the single-GPU candidates.  Here the eight shards run
+    in turn on one GPU and the exchange + merge is done on the host: ids
+    bit-identical to the full head (ties by global id), lse to 1e-6."""
+    s = wl.shape_of(cfg_id)
+    inp, dev = cfg_inputs(cfg_id)
+    y = to_dev(inp["h"])  # any bf16 rows serve: the head alone is compared
+    full_ids, _, full_lse, _ = run_head(s, inp["h"], None, W_dev=dev["W"], with_logits=False)
+    n = 8
+    edges = [s.vocab * g // n for g in range(n + 1)]
+    keys_v, keys_i, lses = [], [], []
+    for g in range(n):
+        v0, v1 = edges[g], edges[g + 1]
+        sub = s.with_(vocab=v1 - v0)
+        cfg = dfs.Config.of(sub)
+        ids = empty((s.rows, s.top_k), torch.int32)
+        lp = empty((s.rows, s.top_k), torch.float32)
+        lse = empty((s.rows,), torch.float32)
+        logits = empty((s.rows, v1 - v0), torch.float32)
+        dfs.head_topk(cfg, y, dev["W"][v0:v1], ids, lp, lse, wsbuf(cfg), logits_f32=logits)
+        torch.cuda.synchronize()
+        ids, lse, logits = from_dev(ids), from_dev(lse), from_dev(logits)
+        # what a shard would send: its candidates' fp32 logits (the keys) with global ids
+        keys_v.append(np.take_along_axis(logits, ids, 1).astype(np.float64))
+        keys_i.append(ids.astype(np.int64) + v0)
+        lses.append(lse.astype(np.float64))
+    V_, I_ = np.concatenate(keys_v, 1), np.concatenate(keys_i, 1)
+    for r in range(s.rows):
+        order = np.lexsort((I_[r], -V_[r]))[: s.top_k]
+        assert list(I_[r, order]) == list(full_ids[r]), r
+    L = np.stack(lses, 1)
+    m = L.max(1)
+    merged = m + np.log(np.exp(L - m[:, None]).sum(1))
+    assert np.max(np.abs(merged - full_lse.astype(np.float64)) / np.abs(full_lse)) <= 1e-6
+
+
 # ============================================================== top-K of given logits
 
 def crafted_logits(rows, V, seed):
