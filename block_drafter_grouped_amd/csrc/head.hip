@@ -293,8 +293,8 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
 // [row][k][chunk], so that threads reading consecutive chunks coalesce.
 // lse = M + log S with (M, S) the combined (max, sum of exp), combined in a
 // fixed order.
-// K > 16 (merge64_kernel): one workgroup (4 waves) per row: a K-round
-// tournament per wave over its 64 chunk lists, then over the 4 wave lists.
+// K > 16 (merge64_kernel, below): the same gather-and-rank with an exact
+// threshold.
 // K <= 16, nch <= 256 (merge16_kernel): one workgroup of 1024 threads per row.  Thread t owns
 // keys 4*(t/256) .. +3 of chunk t%256 (coalesced loads).  The threshold
 // theta is the minimum over 16 groups of the group's largest key, the
@@ -414,51 +414,128 @@ __global__ __launch_bounds__(1024) void merge16_kernel(const uint64_t* __restric
     if (t == 0) lse_out[row] = z;
 }
 
-__global__ __launch_bounds__(256) void merge64_kernel(const uint64_t* __restrict__ part_keys,
-                                                      const float2* __restrict__ part_ms, int nch, int K,
-                                                      int32_t* __restrict__ cand_ids, float* __restrict__ cand_logp,
-                                                      float* __restrict__ lse_out) {
-    constexpr int KL = 64;
-    __shared__ uint64_t tops[4][KL + 1];
-    __shared__ uint64_t fin[KL];
+// K in 17..64, nch <= 256: one workgroup of 1024 threads per row.  Thread t
+// owns keys 16*(t/256) .. +15 of chunk t%256.  The threshold theta is the
+// exact K-th largest of the first 256 partial keys in element-major order
+// (ranked by counting): at least K keys are >= theta.  The keys >= theta are
+// gathered in LDS and ranked; if more than kMergeCap pass (massive ties),
+// theta is raised to the exact K-th largest key by bisection over the
+// 64-bit key range, after which exactly K keys pass.
+constexpr int kMergeCap = 1024;
+
+__global__ __launch_bounds__(1024) void merge64_kernel(const uint64_t* __restrict__ part_keys,
+                                                       const float2* __restrict__ part_ms, int nch, int K,
+                                                       int32_t* __restrict__ cand_ids, float* __restrict__ cand_logp,
+                                                       float* __restrict__ lse_out) {
+    __shared__ uint64_t held[256];
+    __shared__ uint64_t cand[kMergeCap];
+    __shared__ uint64_t fin[64];
     __shared__ float2 wms[4];
-    __shared__ float zsh;
+    __shared__ int wcnt[16];
+    __shared__ int cnt;
+    __shared__ uint64_t theta_sh, top_sh;
+    __shared__ float z_sh;
     const int row = blockIdx.x, t = threadIdx.x;
     const int lane = t & (kWave - 1), wave = t / kWave;
-    const bool have = t < nch;
-    const uint64_t* src = part_keys + (size_t)row * K * nch + (have ? t : 0);
-    uint64_t lst[KL];
+    const int c = t & 255, sub = t >> 8;
+    const uint64_t* base = part_keys + (size_t)row * K * nch;
+    uint64_t k16[16];
 #pragma unroll
-    for (int i = 0; i < KL; ++i) lst[i] = (have && i < K) ? src[(size_t)i * nch] : 0ull;
-    MaxSum x{-INFINITY, 0.f};
-    if (have) {
-        const float2 p = part_ms[(size_t)row * nch + t];
-        x = MaxSum{p.x, p.y};
+    for (int e = 0; e < 16; ++e) {
+        const int i = 16 * sub + e;
+        k16[e] = (c < nch && i < K) ? base[(size_t)i * nch + c] : 0ull;
     }
-    x = wave_ms_reduce(x);
-    if (lane == 0) wms[wave] = make_float2(x.m, x.s);
-    for (int round = 0; round < K; ++round) {
-        const uint64_t mx = wave_max_u64(lst[0]);
-        if (lst[0] == mx && mx != 0ull) {
-#pragma unroll
-            for (int i = 0; i < KL - 1; ++i) lst[i] = lst[i + 1];
-            lst[KL - 1] = 0ull;
+    if (t == 0) {
+        cnt = 0;
+        theta_sh = 0ull;
+        top_sh = 0ull;
+    }
+    if (sub == 0) {  // waves 0-3: the (max, sum) partials and the first 256 keys
+        MaxSum x{-INFINITY, 0.f};
+        if (c < nch) {
+            const float2 p = part_ms[(size_t)row * nch + c];
+            x = MaxSum{p.x, p.y};
         }
-        if (lane == 0) tops[wave][round] = mx;
+        x = wave_ms_reduce(x);
+        if (lane == 0) wms[wave] = make_float2(x.m, x.s);
+        held[t] = t < nch * K ? base[t] : 0ull;
     }
     __syncthreads();
-    if (wave == 0) wave_tournament(&tops[0][0], 4, KL + 1, K, K, fin);
+    if (sub == 0) {
+        const uint64_t hk = held[t];
+        int rank = 0;
+        for (int j = 0; j < 256; ++j) rank += held[j] > hk ? 1 : 0;
+        if (rank == K - 1 && hk != 0ull) theta_sh = hk;  // fewer than K keys: theta stays 0
+        if (rank == 0 && hk != 0ull) top_sh = hk;
+    }
     if (t == 0) {
         MaxSum zz{-INFINITY, 0.f};
         for (int w = 0; w < 4; ++w) zz = ms_combine(zz, MaxSum{wms[w].x, wms[w].y});
-        zsh = (zz.m == -INFINITY) ? -INFINITY : zz.m + logf(zz.s);
+        z_sh = (zz.m == -INFINITY) ? -INFINITY : zz.m + logf(zz.s);
     }
     __syncthreads();
-    const float z = zsh;
-    for (int k = t; k < K; k += blockDim.x) {
-        const uint64_t key = fin[k];
-        cand_ids[(size_t)row * K + k] = key_id(key);
-        cand_logp[(size_t)row * K + k] = key_value(key) - z;
+    uint64_t theta = theta_sh;
+    // The row's largest key: the first 256 element-major keys hold every
+    // chunk head (nch <= 256), so it is the top-ranked one.
+    const uint64_t top = top_sh;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int n = 0;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        int before = 0, total = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint64_t bal = __ballot(k16[e] >= theta && k16[e] != 0ull);
+            before += __popcll(bal & lt);
+            total += __popcll(bal);
+        }
+        int wbase = 0;
+        if (lane == 0 && total > 0) wbase = atomicAdd(&cnt, total);
+        wbase = __shfl(wbase, 0, kWave);
+        __syncthreads();
+        n = cnt;
+        if (n <= kMergeCap) {
+            int p = wbase + before;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (k16[e] >= theta && k16[e] != 0ull) cand[p++] = k16[e];
+            break;
+        }
+        // Too many (massive ties): the exact K-th largest key by bisection;
+        // more than kMergeCap >= K keys are >= theta, so it lies in [theta, top].
+        uint64_t lo = theta, hi = top;
+        while (lo < hi) {
+            const uint64_t mid = lo + (hi - lo) / 2 + 1;
+            int cc = 0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) cc += __popcll(__ballot(k16[e] >= mid));
+            if (lane == 0) wcnt[wave] = cc;
+            __syncthreads();
+            int all = 0;
+            for (int w = 0; w < 16; ++w) all += wcnt[w];
+            __syncthreads();
+            if (all >= K) lo = mid;
+            else hi = mid - 1;
+        }
+        theta = lo;
+        __syncthreads();  // every thread has read cnt
+        if (t == 0) cnt = 0;
+        __syncthreads();
+    }
+    if (n > kMergeCap) n = 0;  // unreachable: exactly K <= kMergeCap keys pass the exact threshold
+    __syncthreads();
+    for (int i = t; i < n; i += blockDim.x) {
+        const uint64_t key = cand[i];
+        int rank = 0;
+        for (int j = 0; j < n; ++j) rank += cand[j] > key ? 1 : 0;
+        if (rank < K) fin[rank] = key;
+    }
+    for (int i = n + t; i < K; i += blockDim.x) fin[i] = 0ull;
+    __syncthreads();
+    const float z = z_sh;
+    if (t < K) {
+        const uint64_t key = fin[t];
+        cand_ids[(size_t)row * K + t] = key_id(key);
+        cand_logp[(size_t)row * K + t] = key_value(key) - z;
     }
     if (t == 0) lse_out[row] = z;
 }
@@ -533,7 +610,7 @@ hipError_t launch_merge(const Dims& d, int nch, const uint64_t* keys, const floa
     if (d.K <= 16)
         merge16_kernel<<<d.rows(), 1024, 0, s>>>(keys, ms, nch, d.K, cand_ids, cand_logp, lse);
     else
-        merge64_kernel<<<d.rows(), 256, 0, s>>>(keys, ms, nch, d.K, cand_ids, cand_logp, lse);
+        merge64_kernel<<<d.rows(), 1024, 0, s>>>(keys, ms, nch, d.K, cand_ids, cand_logp, lse);
     return hipGetLastError();
 }
 

@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kSliceThreads, 4) void slice_topk_kernel(const floa
     for (int i = t; i < n; i += kSliceThreads) {
         const uint64_t key = cand[i];
         int rank = 0;
+#pragma unroll 8
         for (int j = 0; j < n; ++j) rank += cand[j] > key ? 1 : 0;
         if (rank < K) out[(size_t)rank * nsl] = key;
     }
@@ -193,11 +194,15 @@ __global__ __launch_bounds__(kSliceThreads, 4) void slice_topk_kernel(const floa
 
 // Slices of the logits ranked per row: at most kSliceLen values each, at
 // most 256 (the partial buffer's chunk count), and enough (slice, row)
-// workgroups to fill the chip when there are few rows.
+// workgroups to fill the chip when there are few rows -- but no shorter than
+// kSliceMin values, so that every lane group holds values: a slice with
+// fewer occupied groups than K has no threshold and ranks all its values.
+constexpr int kSliceMin = 8 * kSliceThreads;
+
 int logits_slices(const Dims& d) {
     const int64_t need = ((int64_t)d.V + kSliceLen - 1) / kSliceLen;
     const int64_t fill = (2048 + d.rows() - 1) / d.rows();
-    const int64_t most = std::min<int64_t>(256, ((int64_t)d.V + kSliceThreads - 1) / kSliceThreads);
+    const int64_t most = std::min<int64_t>(256, std::max<int64_t>(1, (int64_t)d.V / kSliceMin));
     return (int)std::max<int64_t>(need, std::min<int64_t>(fill, most));
 }
 
