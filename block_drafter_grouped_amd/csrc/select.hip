@@ -11,12 +11,12 @@
 // below.  General path:
 // sel_dots: one workgroup per (draft slot, block) computes the K x K matrix
 //   T_t[j, k] = sum_i P[c_{t-1, j}, i] * H_t[i] * Q[c_{t, k}, i]
-// (c_0 = {anchor}: a 1 x K row) from rows gathered out of P and Q, fp32
-// accumulation.
-// viterbi: one wavefront per block, lane k = candidate k.  The max over
-// predecessors broadcasts delta_{t-1}[j] with v_readlane; the final argmax
-// uses a DPP max and a ballot (lowest lane wins ties).
-// walk: the greedy and sampled walks, one wavefront per block.
+// (c_0 = {anchor}: a 1 x K row) from rows gathered out of P and Q into LDS,
+// fp32 accumulation.
+// walk: one workgroup per block walks the scores (best path, greedy or
+//   sampled) from LDS, with T streamed in ahead of the walk.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -45,177 +45,256 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&out)[8]) {
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
-template <typename T>
+// General transition scores: one workgroup (256 threads) per (draft slot,
+// block).  The slot's predecessor rows of P (times the gate, in fp32) and
+// successor rows of Q are gathered into LDS in chunks of 256 / NB channels,
+// all loads of a chunk in flight together; thread (jb, kb) then accumulates
+// the NB x NB dots j = jb + 16 jj, k = kb + 16 kk from LDS (NB = ceil(K /
+// 16)).  Rows are padded by 4 floats, so the 16 rows a wave reads at one
+// channel sit in distinct banks.  An invalid id gives a zero row (the walk
+// marks such a block).
+template <typename T, int NB>
 __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict__ anchor,
                                                        const int32_t* __restrict__ cand_ids, const T* __restrict__ P,
                                                        const T* __restrict__ Q, const float* __restrict__ gate,
                                                        float* __restrict__ Tout, int B, int K, int r, int V) {
+    constexpr int RWS = 16 * NB;         // staged rows per matrix
+    constexpr int CH = 256 / NB;         // channels per chunk
+    constexpr int PITCH = CH + 4;
+    constexpr int UPR = CH / 8;          // 8-channel units per row
+    __shared__ __attribute__((aligned(16))) float Ps[RWS * PITCH];
+    __shared__ __attribute__((aligned(16))) float Qs[RWS * PITCH];
     const int t = blockIdx.x + 1, b = blockIdx.y;
     const int a = anchor[b];
     if (a < 0 || a >= V) return;
     const int nprev = (t == 1) ? 1 : K;
-    for (int p = threadIdx.x; p < nprev * K; p += blockDim.x) {
-        const int j = p / K, k = p % K;
-        const int pa = (t == 1) ? a : cand_ids[((size_t)b * B + t - 1) * K + j];
-        const int qb = cand_ids[((size_t)b * B + t) * K + k];
-        float acc = 0.f;
-        if (pa >= 0 && pa < V && qb >= 0 && qb < V) {
-            const T* pr = P + (size_t)pa * r;
-            const T* qr = Q + (size_t)qb * r;
-            if (gate) {  // context gate of slot t: (P * H) . Q
-                const float* gr = gate + ((size_t)b * B + t) * r;
-                for (int i = 0; i < r; i += 8) {
-                    float x[8], z[8], g[8];
-                    load8<T>(pr + i, x);
-                    load8<T>(qr + i, z);
-                    load8<float>(gr + i, g);
+    const int tid = threadIdx.x, jb = tid / 16, kb = tid % 16;
+    const float* gr = gate ? gate + ((size_t)b * B + t) * r : nullptr;
+    float acc[NB][NB];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc += (x[e] * g[e]) * z[e];
+    for (int jj = 0; jj < NB; ++jj)
+#pragma unroll
+        for (int kk = 0; kk < NB; ++kk) acc[jj][kk] = 0.f;
+    for (int c0 = 0; c0 < r; c0 += CH) {
+        __syncthreads();  // the previous chunk has been read
+        for (int u = tid; u < RWS * UPR; u += 256) {
+            const int row = u / UPR, part = u % UPR;
+            const int ch = c0 + 8 * part;
+            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (ch < r) {
+                if (row < nprev) {
+                    const int pa = (t == 1) ? a : cand_ids[((size_t)b * B + t - 1) * K + row];
+                    if (pa >= 0 && pa < V) {
+                        load8<T>(P + (size_t)pa * r + ch, x);
+                        if (gr) {  // context gate of slot t: (P * H) . Q
+                            float g[8];
+                            load8<float>(gr + ch, g);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x[e] *= g[e];
+                        }
+                    }
                 }
-            } else {
-                for (int i = 0; i < r; i += 8) {
-                    float x[8], z[8];
-                    load8<T>(pr + i, x);
-                    load8<T>(qr + i, z);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc += x[e] * z[e];
+                if (row < K) {
+                    const int qb = cand_ids[((size_t)b * B + t) * K + row];
+                    if (qb >= 0 && qb < V) load8<T>(Q + (size_t)qb * r + ch, z);
                 }
             }
+            float* pd = Ps + row * PITCH + 8 * part;
+            float* qd = Qs + row * PITCH + 8 * part;
+            *(f32x4*)pd = f32x4{x[0], x[1], x[2], x[3]};
+            *(f32x4*)(pd + 4) = f32x4{x[4], x[5], x[6], x[7]};
+            *(f32x4*)qd = f32x4{z[0], z[1], z[2], z[3]};
+            *(f32x4*)(qd + 4) = f32x4{z[4], z[5], z[6], z[7]};
         }
-        Tout[(((size_t)b * (B - 1) + t - 1) * K + j) * K + k] = acc;
+        __syncthreads();
+#pragma unroll 4
+        for (int i = 0; i < CH; i += 4) {
+            f32x4 pv[NB], qv[NB];
+#pragma unroll
+            for (int jj = 0; jj < NB; ++jj) pv[jj] = *(const f32x4*)(Ps + (jb + 16 * jj) * PITCH + i);
+#pragma unroll
+            for (int kk = 0; kk < NB; ++kk) qv[kk] = *(const f32x4*)(Qs + (kb + 16 * kk) * PITCH + i);
+#pragma unroll
+            for (int jj = 0; jj < NB; ++jj)
+#pragma unroll
+                for (int kk = 0; kk < NB; ++kk)
+                    acc[jj][kk] += pv[jj][0] * qv[kk][0] + pv[jj][1] * qv[kk][1] + pv[jj][2] * qv[kk][2] +
+                                   pv[jj][3] * qv[kk][3];
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj) {
+        const int j = jb + 16 * jj;
+#pragma unroll
+        for (int kk = 0; kk < NB; ++kk) {
+            const int k = kb + 16 * kk;
+            if (j < nprev && k < K) Tout[(((size_t)b * (B - 1) + t - 1) * K + j) * K + k] = acc[jj][kk];
+        }
     }
 }
 
-template <int KM>
-__global__ __launch_bounds__(kWave) void viterbi_kernel(const int32_t* __restrict__ anchor,
-                                                        const int32_t* __restrict__ cand_ids,
-                                                        const float* __restrict__ cand_logp,
-                                                        const float* __restrict__ Tin, int32_t* __restrict__ path,
-                                                        float* __restrict__ path_score, int32_t* __restrict__ path_idx,
-                                                        int B, int K, int V) {
+// The walk over precomputed transition scores, one workgroup per block.
+// Candidates, node scores and uniforms go to LDS first; T streams through a
+// double-buffered LDS ring, kWalkChunk floats (whole slots) per buffer, all
+// four waves fetching the next chunk while wave 0 walks the current one, so
+// the sequential walk never waits on HBM per slot.  Wave 0, lane k =
+// candidate k:
+//  * best path (mode 0): delta_1[k] = cand_logp[1][k] + T_1[0][k];
+//    delta_t[k] = max_j (delta_{t-1}[j] + T_t[j][k]) + cand_logp[t][k], the
+//    lowest j on ties, with delta_{t-1}[j] broadcast by v_readlane; the end
+//    is the lowest k with the largest delta, then the back-pointers.
+//  * greedy / sampled (modes 1, 2; Inco AI post, "lightweight path selector":
+//    take the best successor of the token chosen before, or sample it from
+//    the same scores): after index p of slot t-1 (p = 0, the anchor, at
+//    t = 1), s_k = cand_logp[t][k] + T_t[p][k].  Greedy: the largest s_k,
+//    the lowest k on ties.  Sample: e_k = exp((s_k - max s) / temperature),
+//    prefix sums E_k in lane order, and the smallest k with
+//    E_k > u_t * E_{K-1} (the last candidate if rounding leaves none).
+// Each decision follows the same rule as the fp64 reference, in fp32.  The
+// chosen indices go to LDS; all threads then write the path.
+constexpr int kWalkThreads = 256;
+constexpr int kWalkChunk = 12288;  // 48 KB per buffer; >= 3 slots at K = 64
+constexpr int kWalkPer = kWalkChunk / kWalkThreads;
+
+__global__ __launch_bounds__(kWalkThreads) void walk_kernel(const int32_t* __restrict__ anchor,
+                                                            const int32_t* __restrict__ cand_ids,
+                                                            const float* __restrict__ cand_logp,
+                                                            const float* __restrict__ Tin, int mode, float temperature,
+                                                            const float* __restrict__ uniforms,
+                                                            int32_t* __restrict__ path, float* __restrict__ path_score,
+                                                            int32_t* __restrict__ path_idx, int B, int K, int V) {
+    __shared__ float Tbuf[2][kWalkChunk];
+    __shared__ int32_t Cs[64 * 64];  // slot t, candidate k at t * K + k
+    __shared__ float Ls[64 * 64];
     __shared__ uint8_t bp[64 * 64];
-    const int b = blockIdx.x, lane = threadIdx.x;
+    __shared__ float Us[64];
+    __shared__ int32_t pick_s[64];
+    __shared__ float score_s;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int a = anchor[b];
     bool bad = (a < 0 || a >= V);
-    for (int i = lane; i < (B - 1) * K; i += kWave) {
-        const int id = cand_ids[((size_t)b * B + 1) * K + i];
+    for (int i = tid; i < (B - 1) * K; i += kWalkThreads) {
+        const size_t g = ((size_t)b * B + 1) * K + i;
+        const int id = cand_ids[g];
         bad |= (id < 0 || id >= V);
+        Cs[K + i] = id;
+        Ls[K + i] = cand_logp[g];
     }
-    if (__any(bad)) {
-        for (int t = lane; t < B; t += kWave) {
+    if (mode == 2)
+        for (int t = tid; t < B; t += kWalkThreads) Us[t] = uniforms[(size_t)b * B + t];
+    if (__syncthreads_or(bad)) {
+        for (int t = tid; t < B; t += kWalkThreads) {
             path[(size_t)b * B + t] = -1;
             if (path_idx) path_idx[(size_t)b * B + t] = -1;
         }
-        if (lane == 0) path_score[b] = __int_as_float(0x7FC00000);
+        if (tid == 0) path_score[b] = __int_as_float(0x7FC00000);
         return;
     }
+
     const float* Tb = Tin + (size_t)b * (B - 1) * K * K;
+    const int KK = K * K, nslot = B - 1;
+    const int S = kWalkChunk / KK;  // K <= 64, so S >= 3
+    const int nch = (nslot + S - 1) / S;
+    float reg[kWalkPer];
+    auto fetch = [&](int c) {
+        const float* src = Tb + (size_t)c * S * KK;
+        const int n = min(S, nslot - c * S) * KK;
+#pragma unroll
+        for (int u = 0; u < kWalkPer; ++u) {
+            const int e = tid + kWalkThreads * u;
+            reg[u] = e < n ? src[e] : 0.f;
+        }
+    };
+    auto put = [&](int c) {
+        float* dst = Tbuf[c & 1];
+#pragma unroll
+        for (int u = 0; u < kWalkPer; ++u) dst[tid + kWalkThreads * u] = reg[u];
+    };
+
     const bool on = lane < K;
-    float d = on ? cand_logp[((size_t)b * B + 1) * K + lane] + Tb[lane] : -INFINITY;
-    for (int t = 2; t < B; ++t) {
-        const float* Tt = Tb + (size_t)(t - 1) * K * K;
-        float tc[KM];
-#pragma unroll
-        for (int j = 0; j < KM; ++j) tc[j] = (j < K && on) ? Tt[(size_t)j * K + lane] : 0.f;
-        const float lp = on ? cand_logp[((size_t)b * B + t) * K + lane] : 0.f;
-        float best = -INFINITY;
-        int bj = 0;
-#pragma unroll
-        for (int j = 0; j < KM; ++j) {
-            if (j < K) {
-                const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), j));
-                const float c = dj + tc[j];
-                if (j == 0 || c > best) {
-                    best = c;
-                    bj = j;
+    const int kc = on ? lane : K - 1;  // in-bounds column for idle lanes
+    const float inv_t = 1.f / temperature;
+    float d = -INFINITY, total = 0.f;  // best-path state / walk total
+    int prev = 0;                      // walk state: index chosen at t-1
+    fetch(0);
+    put(0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) fetch(c + 1);
+        if (wave == 0) {
+            const float* Tc = Tbuf[c & 1];
+            const int t_end = min(nslot, (c + 1) * S);
+            for (int t = 1 + c * S; t <= t_end; ++t) {
+                const float* Tt = Tc + (t - 1 - c * S) * KK;
+                const float lp = Ls[t * K + kc];
+                if (mode == 0) {
+                    if (t == 1) {
+                        d = on ? lp + Tt[kc] : -INFINITY;
+                    } else {
+                        float best = -INFINITY;
+                        int bj = 0;
+#pragma unroll 8
+                        for (int j = 0; j < K; ++j) {
+                            const float cj = readlane_f32(d, j) + Tt[j * K + kc];
+                            if (j == 0 || cj > best) {
+                                best = cj;
+                                bj = j;
+                            }
+                        }
+                        d = on ? best + lp : -INFINITY;
+                        if (on) bp[t * K + lane] = (uint8_t)bj;
+                    }
+                } else {
+                    const float sk = on ? lp + Tt[prev * K + kc] : -INFINITY;
+                    const float m = wave_max_f32(sk);
+                    int pick;
+                    if (mode == 1) {
+                        pick = __ffsll((unsigned long long)__ballot(on && sk == m)) - 1;
+                    } else {
+                        float e = on ? __expf((sk - m) * inv_t) : 0.f;
+                        for (int o = 1; o < kWave; o <<= 1) {  // inclusive prefix sum in lane order
+                            const float v = __shfl_up(e, o, kWave);
+                            if (lane >= o) e += v;
+                        }
+                        const float tot = readlane_f32(e, K - 1);
+                        const float target = Us[t] * tot;
+                        const uint64_t over = __ballot(on && e > target);
+                        pick = over ? __ffsll((unsigned long long)over) - 1 : K - 1;
+                    }
+                    total += readlane_f32(sk, pick);
+                    prev = pick;
+                    if (lane == 0) pick_s[t] = pick;
                 }
             }
         }
-        d = on ? best + lp : -INFINITY;
-        if (on) bp[t * 64 + lane] = (uint8_t)bj;
+        if (c + 1 < nch) put(c + 1);
+        __syncthreads();
     }
-    const float mx = wave_max_f32(d);
-    const uint64_t ball = __ballot(on && d == mx);
-    const int kb = __ffsll((unsigned long long)ball) - 1;
-    __syncthreads();
-    if (lane == 0) {
-        int k = kb;
-        for (int t = B - 1; t >= 1; --t) {
-            path[(size_t)b * B + t] = cand_ids[((size_t)b * B + t) * K + k];
-            if (path_idx) path_idx[(size_t)b * B + t] = k;
-            if (t >= 2) k = bp[t * 64 + k];
-        }
-        path[(size_t)b * B] = a;
-        if (path_idx) path_idx[(size_t)b * B] = -1;
-        path_score[b] = mx;
-    }
-}
-
-// The greedy and sampled walks (Inco AI post, "lightweight path selector":
-// take the best successor of the token chosen before, or sample it from the
-// same scores).  One wavefront per block, lane k = candidate k.  At slot t,
-// after index p of slot t-1 (p = 0, the anchor, at t = 1), candidate k
-// scores s_k = cand_logp[t][k] + T_t[p][k].  Greedy: the largest s_k, the
-// lowest k on ties.  Sample: e_k = exp((s_k - max s) / temperature), prefix
-// sums E_k in lane order, and the smallest k with E_k > u_t * E_{K-1} (the
-// last candidate if rounding leaves none), u_t = uniforms[b, t].  Each
-// decision follows the same rule as the fp64 reference, in fp32.
-__global__ __launch_bounds__(kWave) void walk_kernel(const int32_t* __restrict__ anchor,
-                                                     const int32_t* __restrict__ cand_ids,
-                                                     const float* __restrict__ cand_logp, const float* __restrict__ Tin,
-                                                     int sample, float temperature, const float* __restrict__ uniforms,
-                                                     int32_t* __restrict__ path, float* __restrict__ path_score,
-                                                     int32_t* __restrict__ path_idx, int B, int K, int V) {
-    const int b = blockIdx.x, lane = threadIdx.x;
-    const int a = anchor[b];
-    bool bad = (a < 0 || a >= V);
-    for (int i = lane; i < (B - 1) * K; i += kWave) {
-        const int id = cand_ids[((size_t)b * B + 1) * K + i];
-        bad |= (id < 0 || id >= V);
-    }
-    if (__any(bad)) {
-        for (int t = lane; t < B; t += kWave) {
-            path[(size_t)b * B + t] = -1;
-            if (path_idx) path_idx[(size_t)b * B + t] = -1;
-        }
-        if (lane == 0) path_score[b] = __int_as_float(0x7FC00000);
-        return;
-    }
-    const float* Tb = Tin + (size_t)b * (B - 1) * K * K;
-    const bool on = lane < K;
-    const float inv_t = 1.f / temperature;
-    int prev = 0;
-    float total = 0.f;
-    for (int t = 1; t < B; ++t) {
-        const float sk = on ? cand_logp[((size_t)b * B + t) * K + lane] + Tb[((size_t)(t - 1) * K + prev) * K + lane]
-                            : -INFINITY;
-        const float m = wave_max_f32(sk);
-        int pick;
-        if (!sample) {
-            pick = __ffsll((unsigned long long)__ballot(on && sk == m)) - 1;
-        } else {
-            float e = on ? __expf((sk - m) * inv_t) : 0.f;
-            for (int o = 1; o < kWave; o <<= 1) {  // inclusive prefix sum in lane order
-                const float v = __shfl_up(e, o, kWave);
-                if (lane >= o) e += v;
+    if (wave == 0) {
+        if (mode == 0) {
+            const float mx = wave_max_f32(d);
+            const uint64_t ball = __ballot(on && d == mx);
+            const int kb = __ffsll((unsigned long long)ball) - 1;
+            if (lane == 0) {
+                int k = kb;
+                for (int t = B - 1; t >= 1; --t) {
+                    pick_s[t] = k;
+                    if (t >= 2) k = bp[t * K + k];
+                }
+                score_s = mx;
             }
-            const float tot = readlane_f32(e, K - 1);
-            const float target = uniforms[(size_t)b * B + t] * tot;
-            const uint64_t over = __ballot(on && e > target);
-            pick = over ? __ffsll((unsigned long long)over) - 1 : K - 1;
-        }
-        total += readlane_f32(sk, pick);
-        prev = pick;
-        if (lane == 0) {
-            path[(size_t)b * B + t] = cand_ids[((size_t)b * B + t) * K + pick];
-            if (path_idx) path_idx[(size_t)b * B + t] = pick;
+        } else if (lane == 0) {
+            score_s = total;
         }
     }
-    if (lane == 0) {
-        path[(size_t)b * B] = a;
-        if (path_idx) path_idx[(size_t)b * B] = -1;
-        path_score[b] = total;
+    __syncthreads();
+    for (int t = tid; t < B; t += kWalkThreads) {
+        const int k = t == 0 ? -1 : pick_s[t];
+        path[(size_t)b * B + t] = t == 0 ? a : Cs[t * K + k];
+        if (path_idx) path_idx[(size_t)b * B + t] = k;
     }
+    if (tid == 0) path_score[b] = score_s;
 }
 
 // Transition scores and the walk of one block, from candidates already in
@@ -351,23 +430,25 @@ hipError_t launch_select(const Dims& d, const SelectOpts& o, const int32_t* anch
     const WsLayout L = ws_layout(d);
     float* T = (float*)(ws + L.T);
     dim3 grid(d.B - 1, d.batch);
-    if (d.bf16)
-        sel_dots_kernel<uint16_t><<<grid, 256, 0, s>>>(anchor, cand_ids, (const uint16_t*)P, (const uint16_t*)Q,
-                                                       o.gate, T, d.B, d.K, d.r, d.V);
+    auto dots = [&](auto nb) {
+        constexpr int NB = decltype(nb)::value;
+        if (d.bf16)
+            sel_dots_kernel<uint16_t, NB><<<grid, 256, 0, s>>>(anchor, cand_ids, (const uint16_t*)P,
+                                                               (const uint16_t*)Q, o.gate, T, d.B, d.K, d.r, d.V);
+        else
+            sel_dots_kernel<float, NB><<<grid, 256, 0, s>>>(anchor, cand_ids, (const float*)P, (const float*)Q,
+                                                            o.gate, T, d.B, d.K, d.r, d.V);
+    };
+    if (d.K <= 16)
+        dots(std::integral_constant<int, 1>{});
+    else if (d.K <= 32)
+        dots(std::integral_constant<int, 2>{});
     else
-        sel_dots_kernel<float><<<grid, 256, 0, s>>>(anchor, cand_ids, (const float*)P, (const float*)Q, o.gate, T,
-                                                    d.B, d.K, d.r, d.V);
+        dots(std::integral_constant<int, 4>{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (o.walk != 0)
-        walk_kernel<<<d.batch, kWave, 0, s>>>(anchor, cand_ids, cand_logp, T, o.walk == 2, o.temperature, o.uniforms,
-                                              path, path_score, path_idx, d.B, d.K, d.V);
-    else if (d.K <= 16)
-        viterbi_kernel<16><<<d.batch, kWave, 0, s>>>(anchor, cand_ids, cand_logp, T, path, path_score, path_idx, d.B,
-                                                     d.K, d.V);
-    else
-        viterbi_kernel<64><<<d.batch, kWave, 0, s>>>(anchor, cand_ids, cand_logp, T, path, path_score, path_idx, d.B,
-                                                     d.K, d.V);
+    walk_kernel<<<d.batch, kWalkThreads, 0, s>>>(anchor, cand_ids, cand_logp, T, o.walk, o.temperature, o.uniforms,
+                                                 path, path_score, path_idx, d.B, d.K, d.V);
     return hipGetLastError();
 }
 

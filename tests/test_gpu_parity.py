@@ -366,6 +366,10 @@ SELECT_SHAPES = [
     S(batch=2, block=64, vocab=9000, top_k=64, rank=64),
     S(batch=5, block=16, vocab=2000, top_k=16, rank=256, dtype="f32"),
     S(batch=3, block=5, vocab=4000, top_k=33, rank=8),
+    # the walk streams T through LDS in whole-slot chunks (42 slots at K 17,
+    # 5 at K 48): several chunks with a ragged last one
+    S(batch=2, block=64, vocab=3000, top_k=17, rank=40),
+    S(batch=3, block=40, vocab=6000, top_k=48, rank=24, dtype="f32"),
 ]
 
 
@@ -527,7 +531,7 @@ def check_walk(s, ids, lp, P, Q, anchor, pidx, score, walk, temperature=1.0, uni
             assert abs(score[b] - sc) <= SCORE_TOL, b
 
 
-@pytest.mark.parametrize("s", SELECT_SHAPES[:4] + GATE_SHAPES[2:], ids=str)
+@pytest.mark.parametrize("s", SELECT_SHAPES[:4] + SELECT_SHAPES[6:] + GATE_SHAPES[2:], ids=str)
 def test_select_greedy_fed(s):
     ids, lp, P, Q, anchor = select_inputs(s, 81 + s.block)
     path, score, pidx = run_select_opts(s, ids, lp, P, Q, anchor, walk="greedy")
@@ -536,7 +540,7 @@ def test_select_greedy_fed(s):
 
 
 @pytest.mark.parametrize("temperature", [0.5, 1.0, 3.0])
-@pytest.mark.parametrize("s", [SELECT_SHAPES[0], SELECT_SHAPES[3], GATE_SHAPES[2]], ids=str)
+@pytest.mark.parametrize("s", [SELECT_SHAPES[0], SELECT_SHAPES[3], SELECT_SHAPES[7], GATE_SHAPES[2]], ids=str)
 def test_select_sample_fed(s, temperature):
     ids, lp, P, Q, anchor = select_inputs(s, 91 + s.block)
     u = np.random.default_rng(92).random((s.batch, s.block)).astype(np.float32)
