@@ -137,17 +137,16 @@ __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict
 // The walk over precomputed transition scores, one workgroup per block.
 // Candidates, node scores and uniforms go to LDS first; T streams through a
 // double-buffered LDS ring, kWalkChunk floats (whole slots) per buffer, all
-// four waves fetching the next chunk while wave 0 walks the current one, so
-// the sequential walk never waits on HBM per slot.  Wave 0, lane k =
-// candidate k:
-//  * best path (mode 0): delta_1[k] = cand_logp[1][k] + T_1[0][k];
-//    delta_t[k] = max_j (delta_{t-1}[j] + T_t[j][k]) + cand_logp[t][k], the
-//    lowest j on ties, with delta_{t-1}[j] broadcast by v_readlane; the end
-//    is the lowest k with the largest delta, then the back-pointers.
+// four waves fetching the next chunk while the current one is walked, so
+// the sequential walk never waits on HBM per slot.  Lane k = candidate k:
+//  * best path (mode 0), all four waves: delta_1[k] = cand_logp[1][k] +
+//    T_1[0][k]; delta_t[k] = max_j (delta_{t-1}[j] + T_t[j][k]) +
+//    cand_logp[t][k], the lowest j on ties; the end is the lowest k with the
+//    largest delta, then the back-pointers.
 //  * greedy / sampled (modes 1, 2; Inco AI post, "lightweight path selector":
 //    take the best successor of the token chosen before, or sample it from
-//    the same scores): after index p of slot t-1 (p = 0, the anchor, at
-//    t = 1), s_k = cand_logp[t][k] + T_t[p][k].  Greedy: the largest s_k,
+//    the same scores), wave 0: after index p of slot t-1 (p = 0, the anchor,
+//    at t = 1), s_k = cand_logp[t][k] + T_t[p][k].  Greedy: the largest s_k,
 //    the lowest k on ties.  Sample: e_k = exp((s_k - max s) / temperature),
 //    prefix sums E_k in lane order, and the smallest k with
 //    E_k > u_t * E_{K-1} (the last candidate if rounding leaves none).
@@ -169,6 +168,9 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const int32_t* __res
     __shared__ float Ls[64 * 64];
     __shared__ uint8_t bp[64 * 64];
     __shared__ float Us[64];
+    __shared__ float dsh[64];  // delta of the previous slot (best path)
+    __shared__ float pv[kWalkThreads / kWave][64];
+    __shared__ int32_t pj[kWalkThreads / kWave][64];
     __shared__ int32_t pick_s[64];
     __shared__ float score_s;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -222,50 +224,79 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const int32_t* __res
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         if (c + 1 < nch) fetch(c + 1);
-        if (wave == 0) {
-            const float* Tc = Tbuf[c & 1];
-            const int t_end = min(nslot, (c + 1) * S);
+        const float* Tc = Tbuf[c & 1];
+        const int t_end = min(nslot, (c + 1) * S);
+        if (mode == 0) {
+            // Best path, all four waves: wave w scans predecessors
+            // j = 16w .. 16w + 15 of every candidate (the first, then a strict
+            // comparison), and the four partial results are combined in
+            // wave order with a strict comparison, so the lowest j with the
+            // largest score wins, as in a left-to-right scan.  delta_{t-1}
+            // is read from LDS (dsh).
             for (int t = 1 + c * S; t <= t_end; ++t) {
                 const float* Tt = Tc + (t - 1 - c * S) * KK;
                 const float lp = Ls[t * K + kc];
-                if (mode == 0) {
-                    if (t == 1) {
-                        d = on ? lp + Tt[kc] : -INFINITY;
-                    } else {
-                        float best = -INFINITY;
-                        int bj = 0;
-#pragma unroll 8
-                        for (int j = 0; j < K; ++j) {
-                            const float cj = readlane_f32(d, j) + Tt[j * K + kc];
-                            if (j == 0 || cj > best) {
-                                best = cj;
-                                bj = j;
-                            }
-                        }
-                        d = on ? best + lp : -INFINITY;
-                        if (on) bp[t * K + lane] = (uint8_t)bj;
-                    }
+                if (t == 1) {
+                    d = on ? lp + Tt[kc] : -INFINITY;
                 } else {
-                    const float sk = on ? lp + Tt[prev * K + kc] : -INFINITY;
-                    const float m = wave_max_f32(sk);
-                    int pick;
-                    if (mode == 1) {
-                        pick = __ffsll((unsigned long long)__ballot(on && sk == m)) - 1;
-                    } else {
-                        float e = on ? __expf((sk - m) * inv_t) : 0.f;
-                        for (int o = 1; o < kWave; o <<= 1) {  // inclusive prefix sum in lane order
-                            const float v = __shfl_up(e, o, kWave);
-                            if (lane >= o) e += v;
+                    float bv = -INFINITY;
+                    int bi = kWave;
+                    const int j0 = 16 * wave;
+                    if (j0 < K) {
+                        float cv[16];
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) {
+                            const int j = min(j0 + u, K - 1);
+                            cv[u] = dsh[j] + Tt[j * K + kc];
                         }
-                        const float tot = readlane_f32(e, K - 1);
-                        const float target = Us[t] * tot;
-                        const uint64_t over = __ballot(on && e > target);
-                        pick = over ? __ffsll((unsigned long long)over) - 1 : K - 1;
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) {
+                            const bool gt = (u == 0) | ((j0 + u < K) & (cv[u] > bv));
+                            bv = gt ? cv[u] : bv;
+                            bi = gt ? j0 + u : bi;
+                        }
                     }
-                    total += readlane_f32(sk, pick);
-                    prev = pick;
-                    if (lane == 0) pick_s[t] = pick;
+                    pv[wave][lane] = bv;
+                    pj[wave][lane] = bi;
+                    __syncthreads();  // partials written; dsh no longer read this slot
+                    float best = pv[0][lane];
+                    int bj = pj[0][lane];
+#pragma unroll
+                    for (int w = 1; w < kWalkThreads / kWave; ++w) {
+                        const float v = pv[w][lane];
+                        const bool gt = v > best;
+                        best = gt ? v : best;
+                        bj = gt ? pj[w][lane] : bj;
+                    }
+                    d = on ? best + lp : -INFINITY;
+                    if (wave == 0 && on) bp[t * K + lane] = (uint8_t)bj;
                 }
+                if (wave == 0) dsh[lane] = d;
+                __syncthreads();  // delta_t published; the partials may be rewritten
+            }
+        } else if (wave == 0) {
+            for (int t = 1 + c * S; t <= t_end; ++t) {
+                const float* Tt = Tc + (t - 1 - c * S) * KK;
+                const float lp = Ls[t * K + kc];
+                const float sk = on ? lp + Tt[prev * K + kc] : -INFINITY;
+                const float m = wave_max_f32(sk);
+                int pick;
+                if (mode == 1) {
+                    pick = __ffsll((unsigned long long)__ballot(on && sk == m)) - 1;
+                } else {
+                    float e = on ? __expf((sk - m) * inv_t) : 0.f;
+                    for (int o = 1; o < kWave; o <<= 1) {  // inclusive prefix sum in lane order
+                        const float v = __shfl_up(e, o, kWave);
+                        if (lane >= o) e += v;
+                    }
+                    const float tot = readlane_f32(e, K - 1);
+                    const float target = Us[t] * tot;
+                    const uint64_t over = __ballot(on && e > target);
+                    pick = over ? __ffsll((unsigned long long)over) - 1 : K - 1;
+                }
+                total += readlane_f32(sk, pick);
+                prev = pick;
+                if (lane == 0) pick_s[t] = pick;
             }
         }
         if (c + 1 < nch) put(c + 1);
@@ -338,30 +369,40 @@ __device__ __forceinline__ void select_block_lds(int b, int a, const int32_t (*C
     __syncthreads();
     if (wave != 0) return;
 
-    const bool on = lane < K;
-    float d = on ? Ls[1][lane] + Ts[0][0][lane] : -INFINITY;
+    // Lane 16 g + k: candidate k, predecessors j = 4g .. 4g + 3.  Each lane
+    // scans its four j (the first, then a strict comparison), then two
+    // butterfly steps combine the groups, the lower j winning ties: the
+    // lowest j with the largest score, as a left-to-right scan finds it.
+    // delta[k] ends up in all four lanes of k; lane j (group 0) serves
+    // delta[j] to the next slot.
+    const int k = lane & 15, g = lane >> 4;
+    const bool on = k < K;
+    float d = on ? Ls[1][k] + Ts[0][0][k] : -INFINITY;
     for (int t = 2; t < B; ++t) {
-        float tc[16];
+        float bv = -INFINITY;
+        int bi = 4 * g;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) tc[j] = Ts[t - 1][j][lane & 15];
-        float best = -INFINITY;
-        int bj = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            if (j < K) {
-                const float dj = readlane_f32(d, j);
-                const float c = dj + tc[j];
-                if (j == 0 || c > best) {
-                    best = c;
-                    bj = j;
-                }
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int j = 4 * g + i;
+            const float dj = __shfl(d, j, kWave);
+            const float c = (j < K) ? dj + Ts[t - 1][j][k] : -INFINITY;
+            const bool gt = (i == 0) | (c > bv);
+            bv = gt ? c : bv;
+            bi = gt ? j : bi;
         }
-        d = on ? best + Ls[t][lane & 15] : -INFINITY;
-        if (on) bp[t][lane] = (uint8_t)bj;
+#pragma unroll
+        for (int o = 16; o < kWave; o <<= 1) {
+            const float ov = __shfl_xor(bv, o, kWave);
+            const int oi = __shfl_xor(bi, o, kWave);
+            const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+            bv = take ? ov : bv;
+            bi = take ? oi : bi;
+        }
+        d = on ? bv + Ls[t][k] : -INFINITY;
+        if (on && g == 0) bp[t][k] = (uint8_t)bi;
     }
     const float mx = wave_max_f32(d);
-    const uint64_t ball = __ballot(on && d == mx);
+    const uint64_t ball = __ballot(on && g == 0 && d == mx);
     const int kb = __ffsll((unsigned long long)ball) - 1;
     if (lane == 0) {
         int k = kb;
