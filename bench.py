@@ -108,6 +108,35 @@ def cpu_baseline(s, inp, budget_s: float) -> dict:
             "sample": f"{n} full call(s) of the same workload ({blocks} blocks) in {el:.1f} s; CPU: {cpu_model()}"}
 
 
+def graph_replay_ms(step, stream, steps: int) -> float:
+    """Milliseconds per step when the step is captured once in a HIP graph and
+    replayed ``steps`` times, timed on ``stream``."""
+    import torch
+
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(stream)
+    with torch.cuda.stream(gstream):
+        step(gstream)
+    stream.wait_stream(gstream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gstream):
+        step(gstream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms = g0.elapsed_time(g1) / steps
+    del graph
+    return ms
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +147,9 @@ def main() -> int:
     ap.add_argument("--stage-steps", type=int, default=None, help="calls per stage timing loop")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run 4 plain 1 GiB device copies (counter calibration for profiles)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the graph replay, per-layer conv and vocabulary-shard timings (for profiler runs: "
+                         "their launches of the same kernels at other sizes would mix into per-kernel means)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -169,27 +201,7 @@ def main() -> int:
     # The same step captured once in a HIP graph and replayed K times: the
     # library takes the caller's stream and never allocates or synchronises,
     # so a caller can cut the launch gaps this way.
-    gstream = torch.cuda.Stream()
-    gstream.wait_stream(stream)
-    with torch.cuda.stream(gstream):
-        step(gstream)
-    stream.wait_stream(gstream)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=gstream):
-        step(gstream)
-    torch.cuda.synchronize()
-    for _ in range(3):
-        graph.replay()
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    ms_graph = g0.elapsed_time(g1) / args.steps
-    del graph
+    ms_graph = None if args.no_extras else graph_replay_ms(step, stream, args.steps)
 
     # Per-stage split, each stage timed alone with HIP events on the same stream.
     n_stage = args.stage_steps or args.steps
@@ -206,30 +218,33 @@ def main() -> int:
         return a.elapsed_time(b) / n_stage * 1e3  # us
 
     us_conv = timed(lambda: dfs.conv(cfg, h, wg_cm, y, ws, stream=stream))
-    # One conv per drafter layer: five layers in one dfs_conv_layers call
-    # against five dfs_conv calls (inputs: the workload's tensors repeated).
     NL = 5
-    hL, wgL = h.repeat(NL, 1, 1).contiguous(), wg_cm.repeat(NL, 1, 1).contiguous()
-    yL = torch.empty((NL, s.rows, s.hidden), dtype=tdt, device="cuda")
-    wsL = torch.empty(dfs.conv_layers_workspace_size(cfg, NL), dtype=torch.uint8, device="cuda")
-    us_layers = timed(lambda: dfs.conv_layers(cfg, NL, hL, wgL, yL, wsL, stream=stream))
+    us_layers = us_separate = us_shard = None
+    if not args.no_extras:
+        # One conv per drafter layer: five layers in one dfs_conv_layers call
+        # against five dfs_conv calls (inputs: the workload's tensors repeated).
+        hL, wgL = h.repeat(NL, 1, 1).contiguous(), wg_cm.repeat(NL, 1, 1).contiguous()
+        yL = torch.empty((NL, s.rows, s.hidden), dtype=tdt, device="cuda")
+        wsL = torch.empty(dfs.conv_layers_workspace_size(cfg, NL), dtype=torch.uint8, device="cuda")
+        us_layers = timed(lambda: dfs.conv_layers(cfg, NL, hL, wgL, yL, wsL, stream=stream))
 
-    def separate():
-        for layer in range(NL):
-            dfs.conv(cfg, hL[layer], wgL[layer], yL[layer], ws, stream=stream)
+        def separate():
+            for layer in range(NL):
+                dfs.conv(cfg, hL[layer], wgL[layer], yL[layer], ws, stream=stream)
 
-    us_separate = timed(separate)
-    del hL, wgL, yL, wsL
+        us_separate = timed(separate)
+        del hL, wgL, yL, wsL
     us_head = timed(lambda: dfs.head_topk(cfg, y, W, ids, lp, lse, ws, stream=stream))
     us_sel = timed(lambda: dfs.select(cfg, anchor, ids, lp, P, Q, path, score, ws, stream=stream))
-    # One GPU's share under vocabulary sharding over 8 GPUs: the head + top-K
-    # stage on an eighth of the weight (the merge of the shards' partials is
-    # a few KB per row, left out).
     vs = s.vocab // 8
-    cfg8 = dfs.Config.of(s.with_(vocab=vs))
-    ws8 = torch.empty(dfs.workspace_size(cfg8), dtype=torch.uint8, device="cuda")
-    us_shard = timed(lambda: dfs.head_topk(cfg8, y, W[:vs], ids, lp, lse, ws8, stream=stream))
-    del ws8
+    if not args.no_extras:
+        # One GPU's share under vocabulary sharding over 8 GPUs: the head +
+        # top-K stage on an eighth of the weight (the merge of the shards'
+        # partials is a few KB per row, left out).
+        cfg8 = dfs.Config.of(s.with_(vocab=vs))
+        ws8 = torch.empty(dfs.workspace_size(cfg8), dtype=torch.uint8, device="cuda")
+        us_shard = timed(lambda: dfs.head_topk(cfg8, y, W[:vs], ids, lp, lse, ws8, stream=stream))
+        del ws8
 
     hb = head_stage_bytes(s)
     traffic = recorded_traffic(args.workload)
@@ -272,15 +287,18 @@ def main() -> int:
                    "conv_group_size": s.group, "conv_kernel_size": s.ksize, "parallelism": "none (1 GPU)"},
         "us_per_block": round(ms_step * 1e3 / s.batch, 3),
         "stage_us": {"conv": round(us_conv, 2), "head_topk": round(us_head, 2), "select": round(us_sel, 2)},
-        "conv_layers_us": {"layers": NL, "one_call": round(us_layers, 2), "separate_calls": round(us_separate, 2)},
-        "vocab_shard_of_8": {"vocab": vs, "head_topk_us": round(us_shard, 2),
-                             "GBps": round((vs * s.hidden + s.rows * s.hidden) * (2 if s.dtype == "bf16" else 4)
-                                           / (us_shard * 1e-6) / 1e9, 1)},
+        "conv_layers_us": None if us_layers is None else
+        {"layers": NL, "one_call": round(us_layers, 2), "separate_calls": round(us_separate, 2)},
+        "vocab_shard_of_8": None if us_shard is None else
+        {"vocab": vs, "head_topk_us": round(us_shard, 2),
+         "GBps": round((vs * s.hidden + s.rows * s.hidden) * (2 if s.dtype == "bf16" else 4)
+                       / (us_shard * 1e-6) / 1e9, 1)},
         "block_hbm_frac": round(block_bytes(s) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "head_mfma_frac": round(head_flops(s) / (us_head * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
-        "graph": {"ms_per_step": round(ms_graph, 5), "value": round(s.batch / (ms_graph * 1e-3), 2),
-                  "note": "the same step replayed from one captured HIP graph"},
+        "graph": None if ms_graph is None else
+        {"ms_per_step": round(ms_graph, 5), "value": round(s.batch / (ms_graph * 1e-3), 2),
+         "note": "the same step replayed from one captured HIP graph"},
         "roofline": roof,
         "cpu_baseline": None,
     }
