@@ -226,11 +226,12 @@ typedef struct {
  *                         by the predecessor, Q by the successor
  *  path       [batch, B]  int32 out: path[b, 0] = anchor[b], then one
  *                         candidate id per draft slot
- *  path_score [batch]     fp32 out: delta_{B-1} of the chosen path
+ *  path_score [batch]     fp32 out: the path's score (see above)
  *  path_idx   [batch, B]  int32, optional: path_idx[b, 0] = -1, then the
  *                         chosen candidate index per draft slot
- * A block whose anchor lies outside [0, V) gets path = -1 in every slot,
- * path_idx = -1 and path_score = NaN; the other blocks are unaffected.
+ * A block whose anchor, or any of whose draft-slot candidate ids, lies
+ * outside [0, V) gets path = -1 in every slot, path_idx = -1 and
+ * path_score = NaN; the other blocks are unaffected.
  */
 int dfs_select(const dfs_config* cfg, const dfs_select_opts* opts,
                const int32_t* anchor, const int32_t* cand_ids, const float* cand_logp,

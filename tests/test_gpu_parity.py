@@ -66,6 +66,7 @@ CONV_SHAPES = [
     S(batch=2, block=6, hidden=128, ksize=4, dtype="f32"),
     S(batch=3, block=16, hidden=64, group=64, ksize=2),
     S(batch=2, block=5, hidden=96, ksize=1, dtype="f32"),
+    S(batch=2, block=8, hidden=8192),  # the largest bf16 hidden size
 ]
 
 
@@ -195,6 +196,23 @@ def check_head_fed(s, y_np, W_np, W_dev=None, rows=None):
 def test_head_topk_fed(s):
     inp = wl.make_inputs_for(s, 11, parts=("h", "W"))
     check_head_fed(s, inp["h"], inp["W"])
+
+
+# The limits of the configuration: the largest vocabulary (2^21, K 64: the
+# K > 16 merge over 256 chunk lists) and the largest bf16 hidden size (8192:
+# the streaming head keeps 128 KB of hidden rows in LDS; the GEMM head runs
+# 128 stages per tile).  Checked against the oracle on sampled rows.
+MAX_HEAD_SHAPES = [
+    S(block=4, hidden=64, vocab=1 << 21, top_k=64),
+    S(block=8, hidden=8192, vocab=20000, top_k=16),
+    S(batch=3, block=8, hidden=8192, vocab=20000, top_k=16),
+]
+
+
+@pytest.mark.parametrize("s", MAX_HEAD_SHAPES, ids=str)
+def test_head_topk_fed_max_sizes(s):
+    inp = wl.make_inputs_for(s, 17, parts=("h", "W"))
+    check_head_fed(s, inp["h"], inp["W"], rows=(0, s.rows - 1))
 
 
 @pytest.mark.parametrize("cfg_id", [1, 2])
@@ -370,6 +388,7 @@ SELECT_SHAPES = [
     # 5 at K 48): several chunks with a ragged last one
     S(batch=2, block=64, vocab=3000, top_k=17, rank=40),
     S(batch=3, block=40, vocab=6000, top_k=48, rank=24, dtype="f32"),
+    S(batch=2, block=4, vocab=5000, top_k=16, rank=4096),  # the largest rank
 ]
 
 
