@@ -12,8 +12,10 @@ namespace dfs {
 namespace {
 
 // Top-K keys and (max, sum of exp) of one slice of one row of fp32 logits;
-// one workgroup of 512 threads per (slice, row), K <= 64, several workgroups
-// per CU so that some load while others rank.
+// one workgroup of 512 threads per (slice, row), K <= 64, four workgroups
+// per CU so that some load while others rank (the launch bound caps the
+// registers at 64; the few values that spill cost less than the lost
+// occupancy: 14 % on 256 rows of the page vocabulary).
 //  - Thread t holds 16 values of the slice in registers: with 16-B aligned
 //    rows (V % 4 == 0) the 4-value units t, t + 512, ..., else the values
 //    t, t + 512, ...  Consecutive threads read consecutive addresses.
@@ -21,6 +23,7 @@ namespace {
 //    maxima, distinct keys unless 0 (an empty group).  Their K-th largest,
 //    theta, has at least K keys >= theta in the slice, so every key of the
 //    slice's top K is >= theta; for ordinary data a few dozen keys pass.
+//    The maxima are ranked by counting, wave w counting maxima 8w .. 8w + 7.
 //    The tests run on the float value and id of a key, not on 64-bit keys.
 //  - The passing keys are gathered in LDS and each is placed by its rank
 //    among them.
@@ -46,11 +49,12 @@ __device__ __forceinline__ bool key_ge(float x, uint32_t id, float tv, uint32_t 
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kSliceThreads, 4) void slice_topk_kernel(const float* __restrict__ logits, int V,
+__global__ __launch_bounds__(kSliceThreads, 8) void slice_topk_kernel(const float* __restrict__ logits, int V,
                                                                       int nsl, int K, uint64_t* __restrict__ part_keys,
                                                                       float2* __restrict__ part_ms) {
     constexpr int NWV = kSliceThreads / kWave;
     __shared__ uint64_t gmax[64];
+    __shared__ int gabove[NWV][64];
     __shared__ uint64_t cand[kSliceCap];
     __shared__ float wsum[NWV];
     __shared__ int wcnt[NWV];
@@ -105,11 +109,19 @@ __global__ __launch_bounds__(kSliceThreads, 4) void slice_topk_kernel(const floa
         theta_sh = 0ull;
     }
     __syncthreads();
-    if (wave == 0) {  // lane i ranks group maximum i against the other 63 (register broadcasts)
+    {  // thread (w, i) counts the maxima 8w .. 8w + 7 above group maximum i
+        const uint64_t g = gmax[lane];
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c += gmax[8 * wave + j] > g ? 1 : 0;
+        gabove[wave][lane] = c;
+    }
+    __syncthreads();
+    if (wave == 0) {  // lane i: the rank of group maximum i
         const uint64_t g = gmax[lane];
         int rank = 0;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) rank += readlane_u64(g, i) > g ? 1 : 0;
+        for (int w = 0; w < NWV; ++w) rank += gabove[w][lane];
         if (rank == K - 1 && g != 0ull) theta_sh = g;  // fewer than K non-empty groups: theta stays 0
         if (rank == 0) top_sh = g;                      // unique when g != 0; all-empty slices write 0
     }
