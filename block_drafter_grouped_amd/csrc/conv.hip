@@ -23,21 +23,23 @@ namespace {
 // idle and be bound by per-CU bandwidth.  The D reduction is therefore split
 // over kConvSplit workgroups per tile, whose partial tiles go to the
 // workspace; a second kernel sums them in a fixed order, applies the tap
-// softmax and the causal taps.
+// softmax and the causal taps.  (Eight splits measured slower at 256 rows.)
 constexpr int kConvSplit = 4;
 constexpr int kGenWaves = 4;
 
-// NF MFMA row fragments (16 rows each) per workgroup.  Each wave puts the
-// loads of G k-steps in flight together.
-template <int NF, int G>
+// NC generator-column fragments x NF row fragments (16 each) per
+// workgroup.  Each wave puts the loads of G k-steps in flight together.  A
+// wave's k-range and its MFMA order do not depend on NC or NF, so neither
+// does z.
+template <int NF, int NC, int G>
 __global__ __launch_bounds__(kGenWaves * kWave) void conv_gen_kernel(const uint16_t* __restrict__ h,
                                                                    const uint16_t* __restrict__ wg,
                                                                    float* __restrict__ zpart, int rows, int D,
                                                                    int C) {
     // grid z = layer * kConvSplit + split; layers are independent [rows, D]
     // inputs with their own generator.
-    __shared__ float red[kGenWaves][NF][4][kWave];
-    const int col0 = blockIdx.x * 16;
+    __shared__ float red[kGenWaves][NC][NF][4][kWave];
+    const int col0 = blockIdx.x * 16 * NC;
     const int row0 = blockIdx.y * 16 * NF;
     const int split = blockIdx.z % kConvSplit, layer = blockIdx.z / kConvSplit;
     h += (size_t)layer * rows * D;
@@ -53,20 +55,26 @@ __global__ __launch_bounds__(kGenWaves * kWave) void conv_gen_kernel(const uint1
 
     // MFMA operands: A = generator rows (i = column of z), B = hidden rows
     // (j = row of z); each lane loads 8 consecutive channels of one row.
-    const uint16_t* arow = wg + (size_t)min(col0 + i16, C - 1) * D + 8 * q;
+    // Columns past C read row C - 1 again; their results are dropped.
+    const uint16_t* arow[NC];
+#pragma unroll
+    for (int cf = 0; cf < NC; ++cf) arow[cf] = wg + (size_t)min(col0 + 16 * cf + i16, C - 1) * D + 8 * q;
     const uint16_t* brow[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) brow[f] = h + (size_t)min(row0 + 16 * f + i16, rows - 1) * D + 8 * q;
 
-    f32x4 acc[NF];
+    f32x4 acc[NC][NF];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cf = 0; cf < NC; ++cf)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[cf][f] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = s_beg; s0 < s_end; s0 += G) {
-        bf16x8 av[G], bv[G][NF];
+        bf16x8 av[G][NC], bv[G][NF];
 #pragma unroll
         for (int u = 0; u < G; ++u) {
             const int s = min(s0 + u, s_end - 1);
-            av[u] = *(const bf16x8*)(arow + 32 * s);
+#pragma unroll
+            for (int cf = 0; cf < NC; ++cf) av[u][cf] = *(const bf16x8*)(arow[cf] + 32 * s);
 #pragma unroll
             for (int f = 0; f < NF; ++f)
                 if (f < nf) bv[u][f] = *(const bf16x8*)(brow[f] + 32 * s);
@@ -75,25 +83,31 @@ __global__ __launch_bounds__(kGenWaves * kWave) void conv_gen_kernel(const uint1
         for (int u = 0; u < G; ++u) {
             if (s0 + u < s_end) {
 #pragma unroll
-                for (int f = 0; f < NF; ++f)
-                    if (f < nf) acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][f], acc[f], 0, 0, 0);
+                for (int cf = 0; cf < NC; ++cf)
+#pragma unroll
+                    for (int f = 0; f < NF; ++f)
+                        if (f < nf)
+                            acc[cf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][cf], bv[u][f], acc[cf][f], 0,
+                                                                                 0, 0);
             }
         }
     }
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+    for (int cf = 0; cf < NC; ++cf)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][f][r][lane] = acc[f][r];
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][cf][f][r][lane] = acc[cf][f][r];
     __syncthreads();
     // Sum the waves in order; MFMA output lane l, register r holds
-    // z[col 4*(l/16) + r][row l%16] of its fragment.
-    for (int e = threadIdx.x; e < NF * 4 * kWave; e += kGenWaves * kWave) {
-        const int f = e / (4 * kWave), r = (e / kWave) & 3, ln = e & (kWave - 1);
-        const int row = row0 + 16 * f + (ln & 15), col = col0 + 4 * (ln >> 4) + r;
+    // z[col 4*(l/16) + r][row l%16] of its fragment pair.
+    for (int e = threadIdx.x; e < NC * NF * 4 * kWave; e += kGenWaves * kWave) {
+        const int cf = e / (NF * 4 * kWave), f = (e / (4 * kWave)) % NF, r = (e / kWave) & 3, ln = e & (kWave - 1);
+        const int row = row0 + 16 * f + (ln & 15), col = col0 + 16 * cf + 4 * (ln >> 4) + r;
         if (row >= rows || col >= C) continue;
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kGenWaves; ++w) sum += red[w][f][r][ln];
+        for (int w = 0; w < kGenWaves; ++w) sum += red[w][cf][f][r][ln];
         zpart[((size_t)split * rows + row) * C + col] = sum;
     }
 }
@@ -207,13 +221,17 @@ hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y,
     if (d.bf16) {
         float* zpart = (float*)(ws + ws_layout(d).zpart);
         if (d.rows() <= 16) {
+            // Few rows: 16 generator columns per workgroup, so that enough
+            // workgroups stream the generator.
             dim3 grid((C + 15) / 16, 1, kConvSplit * layers);
-            conv_gen_kernel<1, 8><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
-                                                                    zpart, d.rows(), d.D, C);
+            conv_gen_kernel<1, 1, 8><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
+                                                                       zpart, d.rows(), d.D, C);
         } else {
-            dim3 grid((C + 15) / 16, (d.rows() + 63) / 64, kConvSplit * layers);
-            conv_gen_kernel<4, 4><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
-                                                                    zpart, d.rows(), d.D, C);
+            // Many rows: 64 x 64 tiles of z, so that each hidden row is read
+            // by C / 64 workgroups instead of C / 16.
+            dim3 grid((C + 63) / 64, (d.rows() + 63) / 64, kConvSplit * layers);
+            conv_gen_kernel<4, 4, 4><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
+                                                                       zpart, d.rows(), d.D, C);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
