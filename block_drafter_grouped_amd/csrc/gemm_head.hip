@@ -76,16 +76,18 @@ constexpr bool kGemmStreamW = true;
 
 constexpr int kGemmProducers = 4;  // two W loaders, two hidden-row loaders
 
-// s_waitcnt with at most n vector-memory operations outstanding (n a
-// multiple of 4 up to 48: the counts the producers use).
+// s_waitcnt with at most n vector-memory operations outstanding, n in
+// 0..48 (a larger n waits for all of them, which is always safe).
 __device__ __forceinline__ void wait_vm(int n) {
     switch (n) {
 #define DFS_WAIT_VM(k)                                                                          \
     case k:                                                                                     \
         __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | ((k) & 0xF) | (((k) >> 4) << 14)); \
         break;
-        DFS_WAIT_VM(4) DFS_WAIT_VM(8) DFS_WAIT_VM(12) DFS_WAIT_VM(16) DFS_WAIT_VM(20) DFS_WAIT_VM(24)
-        DFS_WAIT_VM(28) DFS_WAIT_VM(32) DFS_WAIT_VM(36) DFS_WAIT_VM(40) DFS_WAIT_VM(44) DFS_WAIT_VM(48)
+#define DFS_WAIT_VM4(k) DFS_WAIT_VM(k) DFS_WAIT_VM(k + 1) DFS_WAIT_VM(k + 2) DFS_WAIT_VM(k + 3)
+        DFS_WAIT_VM4(1) DFS_WAIT_VM4(5) DFS_WAIT_VM4(9) DFS_WAIT_VM4(13) DFS_WAIT_VM4(17) DFS_WAIT_VM4(21)
+        DFS_WAIT_VM4(25) DFS_WAIT_VM4(29) DFS_WAIT_VM4(33) DFS_WAIT_VM4(37) DFS_WAIT_VM4(41) DFS_WAIT_VM4(45)
+#undef DFS_WAIT_VM4
 #undef DFS_WAIT_VM
         default:
             __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4));
@@ -106,8 +108,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
     constexpr int WI = WBYTES / 1024 / 2;       // load instructions per W producer per stage
     constexpr int YI = YBYTES / 1024 / 2;       // per hidden-row producer per stage
     static_assert(WI * 2048 == WBYTES && YI * 2048 == YBYTES, "whole load instructions per producer");
-    static_assert((RW - 2) * WI <= 48 && (RW - 2) * WI % 4 == 0 && (RY - 2) * YI <= 48 && (RY - 2) * YI % 4 == 0,
-                  "wait counts");
+    static_assert((RW - 2) * WI <= 48 && (RY - 2) * YI <= 48, "wait counts");
     const int c = blockIdx.x;
     const int row_base = blockIdx.y * RP;
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -127,12 +128,24 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
         // L % UPR, i.e. logical unit (L % UPR) ^ f(row).
         const bool wl = wave < NWB + 2;
         const int pw = wl ? wave - NWB : wave - NWB - 2;
+        // W load instructions of this producer in stage g: instruction n
+        // covers tile rows RPI n .. RPI n + RPI - 1 and is skipped when all of
+        // them lie past the range (the last tile of the range).
+        auto w_count = [&](int g) {
+            const int nv = min(kGemmTV, v_end - (v_beg + (g / S) * kGemmTV));
+            int c = 0;
+#pragma unroll
+            for (int i = 0; i < WI; ++i) c += (RPI * (pw + 2 * i) < nv) ? 1 : 0;
+            return c;
+        };
         auto issue_w = [&](int g) {
             const int k0 = (g % S) * KC, v0 = v_beg + (g / S) * kGemmTV;
+            const int nv = min(kGemmTV, v_end - v0);
             const uint32_t base = smem_base + (uint32_t)((g % RW) * WBYTES);
 #pragma unroll
             for (int i = 0; i < WI; ++i) {
                 const int n = pw + 2 * i;
+                if (RPI * n >= nv) continue;  // wave-uniform
                 const int vr = RPI * n + lane / UPR;
                 const int u = (lane % UPR) ^ gemm_swz<KC>(vr);
                 const int v = min(v0 + vr, v_end - 1);  // past the range: re-read its last row (cache hit)
@@ -151,11 +164,14 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
                 dma16<false>(y + (size_t)row * D + k0 + 8 * u, base + n * 1024);
             }
         };
-        const int R = wl ? RW : RY, per = wl ? WI : YI;
+        const int R = wl ? RW : RY;
         for (int g = 0; g < R - 1 && g < total; ++g) wl ? issue_w(g) : issue_y(g);
         for (int g = 0; g < total; ++g) {
-            // stage g landed: at most the later stages' loads outstanding
-            wait_vm(min(R - 2, total - 1 - g) * per);
+            // stage g landed: at most the later stages' loads outstanding (a
+            // wave's loads complete in order)
+            int later = 0;
+            for (int g2 = g + 1; g2 <= min(g + R - 2, total - 1); ++g2) later += wl ? w_count(g2) : YI;
+            wait_vm(later);
             __syncthreads();  // publish stage g; the slot read in stage g - 1 is free
             if (g + R - 1 < total) wl ? issue_w(g + R - 1) : issue_y(g + R - 1);
         }
@@ -180,6 +196,9 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
             for (int r = 0; r < 16; ++r) acc[vb][rb][r] = 0.f;
     int tile = 0, st = 0;
     for (int g = 0; g < total; ++g) {
+        // vocabulary blocks of this wave that hold rows of the range (the
+        // last tile of the range is partial); the others are skipped
+        const int nvb = min(NVB, max(0, (v_end - (v_beg + tile * kGemmTV) - 32 * vw * NVB + 31) / 32));
         __syncthreads();  // stage g published
         const uint4* sw = (const uint4*)(smem + (size_t)(g % RW) * WBYTES);
         const uint4* sy = (const uint4*)(smem + (size_t)RW * WBYTES + (size_t)(g % RY) * YBYTES);
@@ -190,14 +209,17 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
                 bo[rb] = __builtin_bit_cast(bf16x8, sy[gemm_unit<KC>((rw * NRB + rb) * 32 + j, u)]);
-            // Rows past the range hold copies of its last row; their results
-            // are dropped below.
+            // Rows past the range hold copies of its last row, or stale data
+            // where their loads were skipped; each output row depends on its
+            // own weight row only, and those results are dropped below.
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit<KC>((vw * NVB + vb) * 32 + j, u)]);
+                if (vb < nvb) {
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit<KC>((vw * NVB + vb) * 32 + j, u)]);
 #pragma unroll
-                for (int rb = 0; rb < NRB; ++rb)
-                    acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bo[rb], acc[vb][rb], 0, 0, 0);
+                    for (int rb = 0; rb < NRB; ++rb)
+                        acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bo[rb], acc[vb][rb], 0, 0, 0);
+                }
             }
         }
         if (st == S - 1) {
