@@ -95,7 +95,7 @@ __device__ __forceinline__ void wait_vm(int n) {
     }
 }
 
-template <int NWB, int KC, int RW, int RY, int NVB>
+template <int NWB, int KC, int RW, int RY, int NVB, bool RS>
 __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kernel(
     const uint16_t* __restrict__ y, int rows_total, int D, const uint16_t* __restrict__ W, int V, int nch,
     float* __restrict__ logits) {
@@ -152,12 +152,23 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
                 dma16<kGemmStreamW>(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
             }
         };
+        // Hidden-row load instructions of this producer per stage: with RS
+        // (the last row pass is partial), those whose RPI rows all lie past
+        // the last row are skipped.
+        const int ny = RS ? rows_total - row_base : RP;
+        int y_cnt = YI;
+        if (RS) {
+            y_cnt = 0;
+#pragma unroll
+            for (int i = 0; i < YI; ++i) y_cnt += (RPI * (pw + 2 * i) < ny) ? 1 : 0;
+        }
         auto issue_y = [&](int g) {
             const int k0 = (g % S) * KC;
             const uint32_t base = ybase + (uint32_t)((g % RY) * YBYTES);
 #pragma unroll
             for (int i = 0; i < YI; ++i) {
                 const int n = pw + 2 * i;
+                if (RS && RPI * n >= ny) continue;  // wave-uniform
                 const int r = RPI * n + lane / UPR;
                 const int u = (lane % UPR) ^ gemm_swz<KC>(r);
                 const int row = min(row_base + r, rows_total - 1);
@@ -170,7 +181,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
             // stage g landed: at most the later stages' loads outstanding (a
             // wave's loads complete in order)
             int later = 0;
-            for (int g2 = g + 1; g2 <= min(g + R - 2, total - 1); ++g2) later += wl ? w_count(g2) : YI;
+            for (int g2 = g + 1; g2 <= min(g + R - 2, total - 1); ++g2) later += wl ? w_count(g2) : y_cnt;
             wait_vm(later);
             __syncthreads();  // publish stage g; the slot read in stage g - 1 is free
             if (g + R - 1 < total) wl ? issue_w(g + R - 1) : issue_y(g + R - 1);
@@ -186,6 +197,9 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
     constexpr int NRB = 8 / NVB, NVW = 8 / NVB;
     const int j = lane & 31, half = lane >> 5;
     const int vw = wave % NVW, rw = wave / NVW;
+    // row blocks of this wave that hold rows (RS: the last row pass is
+    // partial); the others are skipped
+    const int nrb = RS ? min(NRB, max(0, (rows_total - row_base - 32 * rw * NRB + 31) / 32)) : NRB;
     const bool vec4 = (V & 3) == 0;  // rows of the logits are 16-B aligned
     f32x16 acc[NVB][NRB];
 #pragma unroll
@@ -208,17 +222,19 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
             bf16x8 bo[NRB];
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
-                bo[rb] = __builtin_bit_cast(bf16x8, sy[gemm_unit<KC>((rw * NRB + rb) * 32 + j, u)]);
-            // Rows past the range hold copies of its last row, or stale data
-            // where their loads were skipped; each output row depends on its
-            // own weight row only, and those results are dropped below.
+                if (rb < nrb) bo[rb] = __builtin_bit_cast(bf16x8, sy[gemm_unit<KC>((rw * NRB + rb) * 32 + j, u)]);
+            // Rows past the range (and hidden rows past the last) hold
+            // copies of its last row, or stale data where their loads were
+            // skipped; each output depends on its own weight row and hidden
+            // row only, and those results are dropped below.
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
                 if (vb < nvb) {
                     const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit<KC>((vw * NVB + vb) * 32 + j, u)]);
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb)
-                        acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bo[rb], acc[vb][rb], 0, 0, 0);
+                        if (rb < nrb)
+                            acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bo[rb], acc[vb][rb], 0, 0, 0);
                 }
             }
         }
@@ -294,12 +310,12 @@ __global__ __launch_bounds__(256) void head_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-template <int NWB, int KC, int RW, int RY, int NVB>
+template <int NWB, int KC, int RW, int RY, int NVB, bool RS>
 hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int nch, float* logits, hipStream_t s) {
     constexpr int RP = 32 * NWB;
     constexpr size_t lds = ((size_t)RW * kGemmTV + (size_t)RY * RP) * KC * 2;
     static_assert(lds <= 160 * 1024, "the stage rings must fit in LDS");
-    auto fn = head_gemm_kernel<NWB, KC, RW, RY, NVB>;
+    auto fn = head_gemm_kernel<NWB, KC, RW, RY, NVB, RS>;
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid(nch, (d.rows() + RP - 1) / RP);
@@ -309,18 +325,28 @@ hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int n
 }
 
 constexpr int kGemmNVB = 4;  // vocabulary blocks per consumer wave (x 2 row blocks)
+constexpr int kGemmSmallRows = 64;  // at most this many rows: 64-row passes (2 consumer waves)
 
 // More than 8 rows: one pass of the GEMM head per 256 rows instead of one
 // weight stream per 8 rows.
 bool use_gemm_head(const Dims& d) { return d.bf16 && d.rows() > kRowsPass; }
 
+template <int NWB, int KC, int RW, int RY>
+hipError_t launch_head_gemm_rs(const Dims& d, const void* y, const void* W, int nch, float* logits, hipStream_t s) {
+    // row skipping only where the last row pass is partial
+    return d.rows() % (32 * NWB) != 0 ? launch_head_gemm_t<NWB, KC, RW, RY, kGemmNVB, true>(d, y, W, nch, logits, s)
+                                      : launch_head_gemm_t<NWB, KC, RW, RY, kGemmNVB, false>(d, y, W, nch, logits, s);
+}
+
 hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {
     const int nch = head_chunks(d);
-    if (d.D % 64 == 0)
-        return d.rows() <= 128 ? launch_head_gemm_t<4, 64, 3, 2, kGemmNVB>(d, y, W, nch, logits, s)
-                               : launch_head_gemm_t<8, 64, 3, 2, kGemmNVB>(d, y, W, nch, logits, s);
-    return d.rows() <= 128 ? launch_head_gemm_t<4, 32, 6, 4, kGemmNVB>(d, y, W, nch, logits, s)
-                           : launch_head_gemm_t<8, 32, 6, 4, kGemmNVB>(d, y, W, nch, logits, s);
+    if (d.D % 64 == 0) {
+        if (d.rows() <= kGemmSmallRows) return launch_head_gemm_rs<2, 64, 3, 2>(d, y, W, nch, logits, s);
+        return d.rows() <= 128 ? launch_head_gemm_rs<4, 64, 3, 2>(d, y, W, nch, logits, s)
+                               : launch_head_gemm_rs<8, 64, 3, 2>(d, y, W, nch, logits, s);
+    }
+    return d.rows() <= 128 ? launch_head_gemm_rs<4, 32, 6, 4>(d, y, W, nch, logits, s)
+                           : launch_head_gemm_rs<8, 32, 6, 4>(d, y, W, nch, logits, s);
 }
 
 hipError_t launch_head_f32(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {

@@ -148,6 +148,7 @@ HEAD_SHAPES = [
     S(batch=4, block=8, hidden=96, vocab=3001, top_k=16),
     S(batch=20, block=8, hidden=128, vocab=70000, top_k=64),
     S(batch=40, block=8, hidden=64, vocab=5000, top_k=5),
+    S(batch=10, block=10, hidden=128, vocab=3001, top_k=16),  # 100 rows: a partial 128-row pass
 ]
 
 
