@@ -25,6 +25,7 @@ namespace {
 // workspace; a second kernel sums them in a fixed order, applies the tap
 // softmax and the causal taps.  (Eight splits measured slower at 256 rows.)
 constexpr int kConvSplit = 4;
+constexpr int kConvNarrowRows = 64;
 constexpr int kGenWaves = 4;
 
 // NC generator-column fragments x NF row fragments (16 each) per
@@ -225,6 +226,12 @@ hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y,
             // workgroups stream the generator.
             dim3 grid((C + 15) / 16, 1, kConvSplit * layers);
             conv_gen_kernel<1, 1, 8><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
+                                                                       zpart, d.rows(), d.D, C);
+        } else if (d.rows() <= kConvNarrowRows) {
+            // Up to kConvNarrowRows rows: 16 columns x 64 rows, so that enough
+            // workgroups still stream the generator.
+            dim3 grid((C + 15) / 16, (d.rows() + 63) / 64, kConvSplit * layers);
+            conv_gen_kernel<4, 1, 4><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
                                                                        zpart, d.rows(), d.D, C);
         } else {
             // Many rows: 64 x 64 tiles of z, so that each hidden row is read
