@@ -7,7 +7,7 @@
 // section "two additions").  The post's context gate H(h_t) is optional: the
 // caller supplies it, or it is 1.
 //
-// Fast path (bf16 tables, K <= 16, no gate, best-path walk): select_fused_kernel,
+// Fast path (bf16 tables, K <= 16, r % 32 == 0, no gate; any walk): select_fused_kernel,
 // below.  General path:
 // sel_dots: one workgroup per (draft slot, block) computes the K x K matrix
 //   T_t[j, k] = sum_i P[c_{t-1, j}, i] * H_t[i] * Q[c_{t, k}, i]
@@ -337,10 +337,11 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const int32_t* __res
 // every gather of a slot in flight at once; wave 0 then walks.
 template <int NWS>
 __device__ __forceinline__ void select_block_lds(int b, int a, const int32_t (*Cs)[16], const float (*Ls)[16],
-                                                 float (*Ts)[16][16], uint8_t (*bp)[16],
-                                                 const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
-                                                 int32_t* __restrict__ path, float* __restrict__ path_score,
-                                                 int32_t* __restrict__ path_idx, int B, int K, int r) {
+                                                 float (*Ts)[16][16], uint8_t (*bp)[16], int mode, float inv_t,
+                                                 const float* Us, const uint16_t* __restrict__ P,
+                                                 const uint16_t* __restrict__ Q, int32_t* __restrict__ path,
+                                                 float* __restrict__ path_score, int32_t* __restrict__ path_idx,
+                                                 int B, int K, int r) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int i16 = lane & 15, q = lane >> 4, kk = min(i16, K - 1);
     const int nks = r / 32;
@@ -368,6 +369,45 @@ __device__ __forceinline__ void select_block_lds(int b, int a, const int32_t (*C
     }
     __syncthreads();
     if (wave != 0) return;
+
+    if (mode != 0) {
+        // Greedy / sampled walk (modes 1, 2), with the rules and arithmetic
+        // of walk_kernel, on the tiles in LDS: lane k = candidate k.
+        const bool on = lane < K;
+        const int k = lane & 15;
+        int prev = 0;
+        float total = 0.f;
+        for (int t = 1; t < B; ++t) {
+            const float sk = on ? Ls[t][k] + Ts[t - 1][prev][k] : -INFINITY;
+            const float m = wave_max_f32(sk);
+            int pick;
+            if (mode == 1) {
+                pick = __ffsll((unsigned long long)__ballot(on && sk == m)) - 1;
+            } else {
+                float e = on ? __expf((sk - m) * inv_t) : 0.f;
+                for (int o = 1; o < kWave; o <<= 1) {  // inclusive prefix sum in lane order
+                    const float v = __shfl_up(e, o, kWave);
+                    if (lane >= o) e += v;
+                }
+                const float tot = readlane_f32(e, K - 1);
+                const float target = Us[t] * tot;
+                const uint64_t over = __ballot(on && e > target);
+                pick = over ? __ffsll((unsigned long long)over) - 1 : K - 1;
+            }
+            total += readlane_f32(sk, pick);
+            prev = pick;
+            if (lane == 0) {
+                path[(size_t)b * B + t] = Cs[t][pick];
+                if (path_idx) path_idx[(size_t)b * B + t] = pick;
+            }
+        }
+        if (lane == 0) {
+            path[(size_t)b * B] = a;
+            if (path_idx) path_idx[(size_t)b * B] = -1;
+            path_score[b] = total;
+        }
+        return;
+    }
 
     // Lane 16 g + k: candidate k, predecessors j = 4g .. 4g + 3.  Each lane
     // scans its four j (the first, then a strict comparison), then two
@@ -425,14 +465,17 @@ __device__ __forceinline__ void write_bad_block(int b, int B, int32_t* path, flo
     if (threadIdx.x == 0) path_score[b] = __int_as_float(0x7FC00000);
 }
 
-// Selector for bf16 tables with K <= 16 and r % 32 == 0, on given candidates.
+// Selector for bf16 tables with K <= 16, r % 32 == 0 and no gate, on given
+// candidates; any walk (mode 0: best path, 1: greedy, 2: sampled).
 template <int NWS>
 __global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
     const int32_t* __restrict__ anchor, const int32_t* __restrict__ cand_ids, const float* __restrict__ cand_logp,
-    const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, int32_t* __restrict__ path,
-    float* __restrict__ path_score, int32_t* __restrict__ path_idx, int B, int K, int r, int V) {
+    const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, int mode, float temperature,
+    const float* __restrict__ uniforms, int32_t* __restrict__ path, float* __restrict__ path_score,
+    int32_t* __restrict__ path_idx, int B, int K, int r, int V) {
     extern __shared__ float Tsm[];  // [B-1][16][16]
     __shared__ float Ls[64][16];
+    __shared__ float Us[64];
     __shared__ int32_t Cs[64][16];
     __shared__ uint8_t bp[64][16];
     const int b = blockIdx.x, t0 = threadIdx.x;
@@ -445,11 +488,14 @@ __global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
         Cs[t][k] = id;
         Ls[t][k] = cand_logp[((size_t)b * B + t) * K + k];
     }
+    if (mode == 2)
+        for (int t = t0; t < B; t += NWS * kWave) Us[t] = uniforms[(size_t)b * B + t];
     if (__syncthreads_or(bad)) {
         write_bad_block(b, B, path, path_score, path_idx);
         return;
     }
-    select_block_lds<NWS>(b, a, Cs, Ls, (float(*)[16][16])Tsm, bp, P, Q, path, path_score, path_idx, B, K, r);
+    select_block_lds<NWS>(b, a, Cs, Ls, (float(*)[16][16])Tsm, bp, mode, 1.f / temperature, Us, P, Q, path,
+                          path_score, path_idx, B, K, r);
 }
 
 }  // namespace
@@ -457,15 +503,17 @@ __global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
 hipError_t launch_select(const Dims& d, const SelectOpts& o, const int32_t* anchor, const int32_t* cand_ids,
                          const float* cand_logp, const void* P, const void* Q, int32_t* path, float* path_score,
                          int32_t* path_idx, char* ws, hipStream_t s) {
-    const bool plain = !o.gate && o.walk == 0;
-    if (plain && d.bf16 && d.K <= 16 && d.r % 32 == 0) {
+    // The fused kernel gathers each wave's slots one after another: for the
+    // greedy and sampled walks it is the faster path up to 16 slots, for the
+    // best path at every length measured (up to 64).
+    if (!o.gate && d.bf16 && d.K <= 16 && d.r % 32 == 0 && (o.walk == 0 || d.B <= 16)) {
         const size_t lds = (size_t)(d.B - 1) * 16 * 16 * sizeof(float);
         hipError_t e = hipFuncSetAttribute((const void*)select_fused_kernel<8>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         select_fused_kernel<8><<<d.batch, 8 * kWave, lds, s>>>(anchor, cand_ids, cand_logp, (const uint16_t*)P,
-                                                             (const uint16_t*)Q, path, path_score, path_idx, d.B,
-                                                             d.K, d.r, d.V);
+                                                             (const uint16_t*)Q, o.walk, o.temperature, o.uniforms,
+                                                             path, path_score, path_idx, d.B, d.K, d.r, d.V);
         return hipGetLastError();
     }
     const WsLayout L = ws_layout(d);

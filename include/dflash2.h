@@ -189,7 +189,9 @@ typedef enum {
  *  uniforms    DFS_WALK_SAMPLE: [batch, B] fp32 device (else DFS_ERR_NULL):
  *              uniforms[b, t] in [0, 1) draws slot t of block b; column 0 is
  *              not read.  The library draws no random numbers itself.
- * Gated or non-Viterbi calls run the fp32 general selector kernels.
+ * Gated calls, and fp32 tables, K > 16 or r % 32 != 0, run the general
+ * selector kernels (fp32 dot products); the others, with any walk, run one
+ * fused kernel (MFMA dot products, fp32 accumulation).
  */
 typedef struct {
     const float* gate;
