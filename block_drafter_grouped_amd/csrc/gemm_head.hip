@@ -17,9 +17,10 @@ namespace {
 //  - One persistent workgroup per CU owns a contiguous vocabulary range and
 //    walks it in tiles of 256 rows of W against every hidden row, in stages
 //    of KC channels (64 when D % 64 == 0, else 32).
-//  - Producer and consumer waves.  NWB consumer waves each own 32 hidden
-//    rows and all 256 vocabulary rows of the tile (8 accumulator tiles of
-//    32x32); they only read LDS, issue MFMAs and store logits.  Four
+//  - Producer and consumer waves.  The NWB consumer waves split the 256
+//    vocabulary rows x 32 NWB hidden rows of a tile into blocks of NVB x
+//    (8 / NVB) accumulator tiles of 32x32 each; they only read LDS, issue
+//    MFMAs and store logits.  Four
 //    producer waves move the operands by direct global->LDS loads, two for W
 //    (a ring of RW stages) and two for the hidden rows (RY stages; L2
 //    resident, so a shallower ring).  A wave's count of outstanding memory
@@ -36,6 +37,9 @@ namespace {
 //    every group of 16 lanes.
 //  - In the 32x32 output layout a lane holds one hidden row and, per tile,
 //    4 runs of 4 consecutive vocabulary entries, stored as 16-B writes.
+//  - Loads and MFMAs for rows past the work are skipped: weight rows past a
+//    CU's range in its last tile, and (RS) hidden rows past the last row in
+//    a partial row pass.
 // Ranking inside this kernel (a sorted per-lane list) was tried first: the
 // lists of the 64 lanes of a wave take their insertions at different values,
 // so the wave ran nearly every insertion and the epilogue cost about a
