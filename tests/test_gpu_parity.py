@@ -660,6 +660,31 @@ def test_draft_block_e2e_small(s):
     check_block_e2e(s, inp, dev)
 
 
+def random_configs(n, seed=2026):
+    """Seeded small configurations spread over the accepted ranges: both
+    dtypes, one, two or four taps, several group sizes, K on both sides of
+    16, few and many rows, ragged vocabularies."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        hidden = int(rng.choice([32, 64, 96, 128, 160, 192, 256]))
+        group = int(rng.choice([g for g in (4, 8, 16, 32) if hidden % g == 0]))
+        top_k = int(rng.integers(1, 25))
+        out.append(S(batch=int(rng.integers(1, 7)), block=int(rng.integers(2, 21)), hidden=hidden,
+                     vocab=int(rng.integers(max(top_k, 16), 6001)), top_k=top_k,
+                     rank=int(rng.choice([8, 16, 24, 32, 64])), group=group, ksize=int(rng.choice([1, 2, 4])),
+                     dtype="f32" if rng.random() < 0.25 else "bf16"))
+    return out
+
+
+@pytest.mark.parametrize("s", random_configs(24), ids=str)
+def test_draft_block_random_configs(s):
+    inp = wl.make_inputs_for(s, 23)
+    dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
+    dev["wg_cm"] = to_dev(wg_channel_major(inp["wg"]))
+    check_block_e2e(s, inp, dev)
+
+
 @pytest.mark.parametrize("walk", ["viterbi", "greedy", "sample"])
 def test_draft_block_with_options(walk):
     """The whole block with a context gate and each walk rule, against the
