@@ -551,6 +551,43 @@ def check_walk(s, ids, lp, P, Q, anchor, pidx, score, walk, temperature=1.0, uni
             assert abs(score[b] - sc) <= SCORE_TOL, b
 
 
+def random_select_cases(n, seed=2027):
+    """Seeded selector cases: shape, walk rule, gate on or off; fused and
+    general kernels both get exercised (bf16, K <= 16, r % 32 == 0, no gate,
+    and B <= 16 for greedy and sampled walks, run the fused kernel)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        top_k = int(rng.choice([1, 3, 8, 16, 16, 16, 17, 33, 64]))
+        s = S(batch=int(rng.integers(1, 6)), block=int(rng.integers(2, 40)), vocab=int(rng.integers(2000, 9000)),
+              top_k=top_k, rank=int(rng.choice([8, 32, 64, 96, 256])),
+              dtype="f32" if rng.random() < 0.25 else "bf16")
+        out.append((s, ("viterbi", "greedy", "sample")[i % 3], bool(rng.random() < 0.25), 300 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", random_select_cases(24), ids=lambda c: f"{c[1]}-gate{int(c[2])}-{c[0]}")
+def test_select_random_options(case):
+    s, walk, gated, seed = case
+    ids, lp, P, Q, anchor = select_inputs(s, seed)
+    gate = gate_for(s, seed + 1) if gated else None
+    u = np.random.default_rng(seed + 2).random((s.batch, s.block)).astype(np.float32)
+    extra = dict(temperature=0.7, uniforms=u) if walk == "sample" else {}
+    path, score, pidx = run_select_opts(s, ids, lp, P, Q, anchor, gate=gate, walk=walk, **extra)
+    assert np.all(path[:, 0] == anchor) and np.all(pidx[:, 0] == -1)
+    for b in range(s.batch):
+        assert all(path[b, t] == ids[b * s.block + t, pidx[b, t]] for t in range(1, s.block))
+    if walk == "viterbi":
+        for b in range(s.batch):
+            rs = slice(b * s.block, (b + 1) * s.block)
+            idx, sc, margin = orc.viterbi(lp[rs].astype(np.float64), block_T(s, ids, P, Q, anchor, b, gate))
+            if margin > NEAR_TIE:
+                assert list(pidx[b]) == list(idx), b
+                assert abs(score[b] - sc) <= SCORE_TOL, b
+    else:
+        check_walk(s, ids, lp, P, Q, anchor, pidx, score, walk, 0.7, u if walk == "sample" else None, gate)
+
+
 @pytest.mark.parametrize("s", SELECT_SHAPES[:4] + SELECT_SHAPES[6:] + GATE_SHAPES[2:], ids=str)
 def test_select_greedy_fed(s):
     ids, lp, P, Q, anchor = select_inputs(s, 81 + s.block)
