@@ -35,8 +35,9 @@ namespace {
 //    unit u ^ f(v) with f(v) = (v >> 2) & 3 (4 units) or (v >> 1) & 7 (8
 //    units), so the 32-row operand reads of a wave hit distinct banks in
 //    every group of 16 lanes.
-//  - In the 32x32 output layout a lane holds one hidden row and, per tile,
-//    4 runs of 4 consecutive vocabulary entries, stored as 16-B writes.
+//  - The MFMA takes the hidden rows as its A operand, so in the 32x32 output
+//    layout a lane holds one vocabulary entry of 16 rows: each store
+//    instruction writes whole 128-B lines of two rows.
 //  - Loads and MFMAs for rows past the work are skipped: weight rows past a
 //    CU's range in its last tile, and (RS) hidden rows past the last row in
 //    a partial row pass.
@@ -204,7 +205,6 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
     // row blocks of this wave that hold rows (RS: the last row pass is
     // partial); the others are skipped
     const int nrb = RS ? min(NRB, max(0, (rows_total - row_base - 32 * rw * NRB + 31) / 32)) : NRB;
-    const bool vec4 = (V & 3) == 0;  // rows of the logits are 16-B aligned
     f32x16 acc[NVB][NRB];
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb)
@@ -237,35 +237,35 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
                     const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit<KC>((vw * NVB + vb) * 32 + j, u)]);
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb)
-                        if (rb < nrb)
-                            acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bo[rb], acc[vb][rb], 0, 0, 0);
+                        if (rb < nrb)  // hidden rows as A, weight rows as B: see the store below
+                            acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[rb], a, acc[vb][rb], 0, 0, 0);
                 }
             }
         }
         if (st == S - 1) {
             // Tile done.  For vocabulary block vb and row block rb the lane
-            // holds logit[v][row] in acc[vb][rb][r], with row = its row
-            // block's row j and v = base + 32 vb' + 8 (r / 4) + 4 half + r % 4.
+            // holds logit[v][row] in acc[vb][rb][r], with v = the block's
+            // vocabulary entry j and row = its row 8 (r / 4) + 4 half + r % 4.
+            // One store instruction (fixed vb, rb, r) thus writes 32
+            // consecutive logits of one row from each half-wave: two whole
+            // 128-B lines.  (With the operands the other way round each lane
+            // held one row, and a 16-B store touched 32 lines, 32 B of each.)
+            // Addresses: a wave-uniform base per (row block, vocabulary block,
+            // register) and one lane offset (half-wave row, entry j) for all.
             const int vt = v_beg + tile * kGemmTV;
+            const uint32_t lane_off = (uint32_t)(4 * half * V + j);
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                const int row = row_base + (rw * NRB + rb) * 32 + j;
-                if (row < rows_total) {
-                    float* out = logits + (size_t)row * V;
+                const int row0 = row_base + (rw * NRB + rb) * 32;
 #pragma unroll
-                    for (int vb = 0; vb < NVB; ++vb) {
+                for (int vb = 0; vb < NVB; ++vb) {
+                    const int v0 = vt + 32 * (vw * NVB + vb);
+                    const bool vok = v0 + j < v_end;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int v = vt + 32 * (vw * NVB + vb) + 8 * q + 4 * half;
-                            if (vec4 && v + 3 < v_end) {
-                                *(f32x4*)(out + v) = f32x4{acc[vb][rb][4 * q], acc[vb][rb][4 * q + 1],
-                                                           acc[vb][rb][4 * q + 2], acc[vb][rb][4 * q + 3]};
-                            } else {
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    if (v + e < v_end) out[v + e] = acc[vb][rb][4 * q + e];
-                            }
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int rt = 8 * (r >> 2) + (r & 3);
+                        float* base = logits + ((size_t)(row0 + rt) * V + v0);
+                        if (vok && row0 + rt + 4 * half < rows_total) base[lane_off] = acc[vb][rb][r];
                     }
                 }
             }
