@@ -9,14 +9,13 @@
 //
 // Fast path (bf16 tables, K <= 16, r % 32 == 0, no gate; any walk): select_fused_kernel,
 // below.  General path:
-// sel_dots: one workgroup per (draft slot, block) computes the K x K matrix
+// sel_dots: one workgroup per (draft slot, block, 16 x 16 sub-tile) computes
+// the K x K matrix
 //   T_t[j, k] = sum_i P[c_{t-1, j}, i] * H_t[i] * Q[c_{t, k}, i]
 // (c_0 = {anchor}: a 1 x K row) from rows gathered out of P and Q into LDS,
 // fp32 accumulation.
 // walk: one workgroup per block walks the scores (best path, greedy or
 //   sampled) from LDS, with T streamed in ahead of the walk.
-#include <type_traits>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -46,45 +45,44 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&out)[8]) {
 }
 
 // General transition scores: one workgroup (256 threads) per (draft slot,
-// block).  The slot's predecessor rows of P (times the gate, in fp32) and
-// successor rows of Q are gathered into LDS in chunks of 256 / NB channels,
-// all loads of a chunk in flight together; thread (jb, kb) then accumulates
-// the NB x NB dots j = jb + 16 jj, k = kb + 16 kk from LDS (NB = ceil(K /
-// 16)).  Rows are padded by 4 floats, so the 16 rows a wave reads at one
-// channel sit in distinct banks.  An invalid id gives a zero row (the walk
-// marks such a block).
-template <typename T, int NB>
+// block, 16 x 16 sub-tile of the K x K matrix).  The sub-tile's 16
+// predecessor rows of P (times the gate, in fp32) and 16 successor rows of Q
+// are gathered into LDS in chunks of 256 channels, all loads of a chunk in
+// flight together; thread (jb, kb) then accumulates the dot j = j0 + jb,
+// k = k0 + kb from LDS.  Rows are padded by 4 floats, so the 16 rows a wave
+// reads at one channel sit in distinct banks.  An invalid id gives a zero
+// row (the walk marks such a block).
+constexpr int kDotsCh = 256;
+constexpr int kDotsPitch = kDotsCh + 4;
+
+template <typename T>
 __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict__ anchor,
                                                        const int32_t* __restrict__ cand_ids, const T* __restrict__ P,
                                                        const T* __restrict__ Q, const float* __restrict__ gate,
                                                        float* __restrict__ Tout, int B, int K, int r, int V) {
-    constexpr int RWS = 16 * NB;         // staged rows per matrix
-    constexpr int CH = 256 / NB;         // channels per chunk
-    constexpr int PITCH = CH + 4;
-    constexpr int UPR = CH / 8;          // 8-channel units per row
-    __shared__ __attribute__((aligned(16))) float Ps[RWS * PITCH];
-    __shared__ __attribute__((aligned(16))) float Qs[RWS * PITCH];
+    constexpr int UPR = kDotsCh / 8;  // 8-channel units per row
+    __shared__ __attribute__((aligned(16))) float Ps[16 * kDotsPitch];
+    __shared__ __attribute__((aligned(16))) float Qs[16 * kDotsPitch];
     const int t = blockIdx.x + 1, b = blockIdx.y;
+    const int nb = (K + 15) / 16;
+    const int j0 = 16 * (blockIdx.z / nb), k0 = 16 * (blockIdx.z % nb);
     const int a = anchor[b];
-    if (a < 0 || a >= V) return;
     const int nprev = (t == 1) ? 1 : K;
+    if (a < 0 || a >= V || j0 >= nprev) return;  // uniform
     const int tid = threadIdx.x, jb = tid / 16, kb = tid % 16;
     const float* gr = gate ? gate + ((size_t)b * B + t) * r : nullptr;
-    float acc[NB][NB];
-#pragma unroll
-    for (int jj = 0; jj < NB; ++jj)
-#pragma unroll
-        for (int kk = 0; kk < NB; ++kk) acc[jj][kk] = 0.f;
-    for (int c0 = 0; c0 < r; c0 += CH) {
+    float acc = 0.f;
+    for (int c0 = 0; c0 < r; c0 += kDotsCh) {
         __syncthreads();  // the previous chunk has been read
-        for (int u = tid; u < RWS * UPR; u += 256) {
+        for (int u = tid; u < 16 * UPR; u += 256) {
             const int row = u / UPR, part = u % UPR;
             const int ch = c0 + 8 * part;
             float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             if (ch < r) {
-                if (row < nprev) {
-                    const int pa = (t == 1) ? a : cand_ids[((size_t)b * B + t - 1) * K + row];
+                const int j = j0 + row, k = k0 + row;
+                if (j < nprev) {
+                    const int pa = (t == 1) ? a : cand_ids[((size_t)b * B + t - 1) * K + j];
                     if (pa >= 0 && pa < V) {
                         load8<T>(P + (size_t)pa * r + ch, x);
                         if (gr) {  // context gate of slot t: (P * H) . Q
@@ -95,13 +93,13 @@ __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict
                         }
                     }
                 }
-                if (row < K) {
-                    const int qb = cand_ids[((size_t)b * B + t) * K + row];
+                if (k < K) {
+                    const int qb = cand_ids[((size_t)b * B + t) * K + k];
                     if (qb >= 0 && qb < V) load8<T>(Q + (size_t)qb * r + ch, z);
                 }
             }
-            float* pd = Ps + row * PITCH + 8 * part;
-            float* qd = Qs + row * PITCH + 8 * part;
+            float* pd = Ps + row * kDotsPitch + 8 * part;
+            float* qd = Qs + row * kDotsPitch + 8 * part;
             *(f32x4*)pd = f32x4{x[0], x[1], x[2], x[3]};
             *(f32x4*)(pd + 4) = f32x4{x[4], x[5], x[6], x[7]};
             *(f32x4*)qd = f32x4{z[0], z[1], z[2], z[3]};
@@ -109,29 +107,14 @@ __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict
         }
         __syncthreads();
 #pragma unroll 4
-        for (int i = 0; i < CH; i += 4) {
-            f32x4 pv[NB], qv[NB];
-#pragma unroll
-            for (int jj = 0; jj < NB; ++jj) pv[jj] = *(const f32x4*)(Ps + (jb + 16 * jj) * PITCH + i);
-#pragma unroll
-            for (int kk = 0; kk < NB; ++kk) qv[kk] = *(const f32x4*)(Qs + (kb + 16 * kk) * PITCH + i);
-#pragma unroll
-            for (int jj = 0; jj < NB; ++jj)
-#pragma unroll
-                for (int kk = 0; kk < NB; ++kk)
-                    acc[jj][kk] += pv[jj][0] * qv[kk][0] + pv[jj][1] * qv[kk][1] + pv[jj][2] * qv[kk][2] +
-                                   pv[jj][3] * qv[kk][3];
+        for (int i = 0; i < kDotsCh; i += 4) {
+            const f32x4 pv = *(const f32x4*)(Ps + jb * kDotsPitch + i);
+            const f32x4 qv = *(const f32x4*)(Qs + kb * kDotsPitch + i);
+            acc += pv[0] * qv[0] + pv[1] * qv[1] + pv[2] * qv[2] + pv[3] * qv[3];
         }
     }
-#pragma unroll
-    for (int jj = 0; jj < NB; ++jj) {
-        const int j = jb + 16 * jj;
-#pragma unroll
-        for (int kk = 0; kk < NB; ++kk) {
-            const int k = kb + 16 * kk;
-            if (j < nprev && k < K) Tout[(((size_t)b * (B - 1) + t - 1) * K + j) * K + k] = acc[jj][kk];
-        }
-    }
+    const int j = j0 + jb, k = k0 + kb;
+    if (j < nprev && k < K) Tout[(((size_t)b * (B - 1) + t - 1) * K + j) * K + k] = acc;
 }
 
 // The walk over precomputed transition scores, one workgroup per block.
@@ -518,22 +501,14 @@ hipError_t launch_select(const Dims& d, const SelectOpts& o, const int32_t* anch
     }
     const WsLayout L = ws_layout(d);
     float* T = (float*)(ws + L.T);
-    dim3 grid(d.B - 1, d.batch);
-    auto dots = [&](auto nb) {
-        constexpr int NB = decltype(nb)::value;
-        if (d.bf16)
-            sel_dots_kernel<uint16_t, NB><<<grid, 256, 0, s>>>(anchor, cand_ids, (const uint16_t*)P,
-                                                               (const uint16_t*)Q, o.gate, T, d.B, d.K, d.r, d.V);
-        else
-            sel_dots_kernel<float, NB><<<grid, 256, 0, s>>>(anchor, cand_ids, (const float*)P, (const float*)Q,
-                                                            o.gate, T, d.B, d.K, d.r, d.V);
-    };
-    if (d.K <= 16)
-        dots(std::integral_constant<int, 1>{});
-    else if (d.K <= 32)
-        dots(std::integral_constant<int, 2>{});
+    const int nb = (d.K + 15) / 16;
+    dim3 grid(d.B - 1, d.batch, nb * nb);
+    if (d.bf16)
+        sel_dots_kernel<uint16_t><<<grid, 256, 0, s>>>(anchor, cand_ids, (const uint16_t*)P, (const uint16_t*)Q,
+                                                       o.gate, T, d.B, d.K, d.r, d.V);
     else
-        dots(std::integral_constant<int, 4>{});
+        sel_dots_kernel<float><<<grid, 256, 0, s>>>(anchor, cand_ids, (const float*)P, (const float*)Q, o.gate, T,
+                                                    d.B, d.K, d.r, d.V);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     walk_kernel<<<d.batch, kWalkThreads, 0, s>>>(anchor, cand_ids, cand_logp, T, o.walk, o.temperature, o.uniforms,
