@@ -765,6 +765,52 @@ def test_draft_block_with_options(walk):
     assert walked >= s.batch - 1
 
 
+@pytest.mark.parametrize("case", ["page_batch1", "rows_40", "greedy_b16", "zero_weight"])
+def test_draft_block_equals_separate_calls(case):
+    """dfs_draft_block gives the same bits as dfs_conv, dfs_head_topk and
+    dfs_select called one after another: candidates, scores, path and path
+    score.  The all-zero weight ties every logit, so more keys than the
+    merge's gather holds reach its threshold and its list merge runs."""
+    opts = {}
+    if case == "page_batch1":
+        s = wl.shape_of(2)
+        inp, dev = cfg_inputs(2)
+    else:
+        s = {"rows_40": S(batch=5, block=8, hidden=256, vocab=9001, top_k=16, rank=64),
+             "greedy_b16": S(batch=3, block=16, hidden=128, vocab=7000, top_k=12, rank=32),
+             "zero_weight": S(batch=2, block=8, hidden=128, vocab=5000, top_k=16, rank=64)}[case]
+        inp = wl.make_inputs_for(s, 31)
+        if case == "zero_weight":
+            inp["W"] = np.zeros_like(inp["W"])
+        dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
+        dev["wg_cm"] = to_dev(wg_channel_major(inp["wg"]))
+        if case == "greedy_b16":
+            opts = dict(walk="greedy")
+    cfg = dfs.Config.of(s)
+    path = empty((s.batch, s.block), torch.int32)
+    score = empty((s.batch,), torch.float32)
+    ids = empty((s.rows, s.top_k), torch.int32)
+    lp = empty((s.rows, s.top_k), torch.float32)
+    dfs.draft_block(cfg, dev["h"], dev["anchor"], dev["wg_cm"], dev["W"], dev["P"], dev["Q"], path, score,
+                    wsbuf(cfg), cand_ids=ids, cand_logp=lp, **opts)
+    y = empty((s.rows, s.hidden), torch.int16)
+    ids2 = empty((s.rows, s.top_k), torch.int32)
+    lp2 = empty((s.rows, s.top_k), torch.float32)
+    lse2 = empty((s.rows,), torch.float32)
+    path2 = empty((s.batch, s.block), torch.int32)
+    score2 = empty((s.batch,), torch.float32)
+    dfs.conv(cfg, dev["h"], dev["wg_cm"], y, wsbuf(cfg))
+    dfs.head_topk(cfg, y, dev["W"], ids2, lp2, lse2, wsbuf(cfg))
+    dfs.select(cfg, dev["anchor"], ids2, lp2, dev["P"], dev["Q"], path2, score2, wsbuf(cfg), **opts)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(ids), from_dev(ids2))
+    assert np.array_equal(from_dev(lp), from_dev(lp2))
+    assert np.array_equal(from_dev(path), from_dev(path2))
+    assert np.array_equal(from_dev(score), from_dev(score2))
+    if case == "zero_weight":  # every logit 0: the lowest ids, in order
+        assert np.array_equal(from_dev(ids), np.tile(np.arange(s.top_k, dtype=np.int32), (s.rows, 1)))
+
+
 def test_draft_block_deterministic_and_stream():
     s = wl.shape_of(2)
     inp, dev = cfg_inputs(2)
