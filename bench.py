@@ -137,6 +137,55 @@ def graph_replay_ms(step, stream, steps: int) -> float:
     return ms
 
 
+def batch32_line(s, dev, steps: int) -> dict:
+    """The page drafter shape at batch 32 (256 rows), on the weights W, P, Q
+    and the generator of the current run (same shapes and distributions as
+    the batch-32 workload's), with that workload's hidden states and
+    anchors: per-block time and the head stage against the MFMA roofline."""
+    import torch
+
+    import block_drafter_grouped_amd as dfs
+
+    s32 = wl.shape_of(3)
+    if (s.hidden, s.vocab, s.rank, s.top_k, s.block, s.dtype) != (s32.hidden, s32.vocab, s32.rank, s32.top_k,
+                                                                     s32.block, s32.dtype):
+        return None
+    inp = wl.make_inputs_for(s32, 3, parts=("h", "anchor"))
+    h = torch.from_numpy(np.ascontiguousarray(inp["h"]).view(np.int16)).cuda()
+    anchor = torch.from_numpy(inp["anchor"]).cuda()
+    cfg = dfs.Config.of(s32)
+    ws = torch.empty(dfs.workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    path = torch.empty((s32.batch, s32.block), dtype=torch.int32, device="cuda")
+    score = torch.empty((s32.batch,), dtype=torch.float32, device="cuda")
+    ids = torch.empty((s32.rows, s32.top_k), dtype=torch.int32, device="cuda")
+    lp = torch.empty((s32.rows, s32.top_k), dtype=torch.float32, device="cuda")
+    lse = torch.empty((s32.rows,), dtype=torch.float32, device="cuda")
+    y = torch.empty((s32.rows, s32.hidden), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n) -> float:
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3  # us
+
+    us_step = timed(lambda: dfs.draft_block(cfg, h, anchor, dev["wg_cm"], dev["W"], dev["P"], dev["Q"], path,
+                                            score, ws), steps)
+    dfs.conv(cfg, h, dev["wg_cm"], y, ws)
+    us_head = timed(lambda: dfs.head_topk(cfg, y, dev["W"], ids, lp, lse, ws), steps)
+    fl = head_flops(s32)
+    return {"workload": WORKLOAD_NAMES[3], "steps": steps, "us_per_block": round(us_step / s32.batch, 3),
+            "blocks_per_s": round(s32.batch / (us_step * 1e-6), 1), "head_topk_us": round(us_head, 2),
+            "head_tflops": round(fl / (us_head * 1e-6) / 1e12, 1),
+            "head_mfma_frac": round(fl / (us_head * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "note": "W, P, Q and the conv generator of this run; h and anchors of the batch-32 workload"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +295,9 @@ def main() -> int:
         us_shard = timed(lambda: dfs.head_topk(cfg8, y, W[:vs], ids, lp, lse, ws8, stream=stream))
         del ws8
 
+    b32 = None if args.no_extras or args.workload == 3 else batch32_line(
+        s, {"W": W, "P": P, "Q": Q, "wg_cm": wg_cm}, max(10, min(args.steps, 50)))
+
     hb = head_stage_bytes(s)
     traffic = recorded_traffic(args.workload)
     traffic_gbs = round(traffic / (us_head * 1e-6) / 1e9, 1) if traffic else None
@@ -299,6 +351,7 @@ def main() -> int:
         "graph": None if ms_graph is None else
         {"ms_per_step": round(ms_graph, 5), "value": round(s.batch / (ms_graph * 1e-3), 2),
          "note": "the same step replayed from one captured HIP graph"},
+        "batch32": b32,
         "roofline": roof,
         "cpu_baseline": None,
     }
