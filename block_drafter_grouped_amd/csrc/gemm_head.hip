@@ -138,10 +138,10 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
         // them lie past the range (the last tile of the range).
         auto w_count = [&](int g) {
             const int nv = min(kGemmTV, v_end - (v_beg + (g / S) * kGemmTV));
-            int c = 0;
+            int cnt = 0;
 #pragma unroll
-            for (int i = 0; i < WI; ++i) c += (RPI * (pw + 2 * i) < nv) ? 1 : 0;
-            return c;
+            for (int i = 0; i < WI; ++i) cnt += (RPI * (pw + 2 * i) < nv) ? 1 : 0;
+            return cnt;
         };
         auto issue_w = [&](int g) {
             const int k0 = (g % S) * KC, v0 = v_beg + (g / S) * kGemmTV;
@@ -197,8 +197,9 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
 
     // Consumers.  Wave w computes NVB vocabulary blocks x NRB row blocks of
     // 32x32 (NVB * NRB = 8): vocabulary blocks NVB * (w % (8 / NVB)) .., row
-    // blocks NRB * (w / (8 / NVB)) ..  Per 16 channels a wave reads NVB + NRB
-    // operand fragments from LDS for 8 MFMAs.
+    // blocks NRB * (w / (8 / NVB)) ..; 8 / NVB waves span the 256 vocabulary
+    // rows, and the NWB waves the 32 NWB hidden rows.  Per 16 channels a wave
+    // reads NVB + NRB operand fragments from LDS for 8 MFMAs.
     constexpr int NRB = 8 / NVB, NVW = 8 / NVB;
     const int j = lane & 31, half = lane >> 5;
     const int vw = wave % NVW, rw = wave / NVW;
