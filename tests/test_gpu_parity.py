@@ -714,7 +714,21 @@ def random_configs(n, seed=2026):
     return out
 
 
-@pytest.mark.parametrize("s", random_configs(24), ids=str)
+def random_long_configs(n, seed=2028):
+    """Seeded configurations with long blocks and large K (B up to 64, K up
+    to 64), few rows, small vocabularies: the general selector end to end."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        top_k = int(rng.integers(8, 65))
+        out.append(S(batch=int(rng.integers(1, 3)), block=int(rng.integers(17, 65)),
+                     hidden=int(rng.choice([64, 128])), vocab=int(rng.integers(max(top_k, 500), 3001)),
+                     top_k=top_k, rank=int(rng.choice([16, 32, 64])), ksize=int(rng.choice([1, 2, 4])),
+                     dtype="f32" if rng.random() < 0.25 else "bf16"))
+    return out
+
+
+@pytest.mark.parametrize("s", random_configs(24) + random_long_configs(8), ids=str)
 def test_draft_block_random_configs(s):
     inp = wl.make_inputs_for(s, 23)
     dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
