@@ -117,6 +117,15 @@ __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict
     if (j < nprev && k < K) Tout[(((size_t)b * (B - 1) + t - 1) * K + j) * K + k] = acc;
 }
 
+// A block whose anchor or candidates are invalid: path -1, score NaN.
+__device__ __forceinline__ void write_bad_block(int b, int B, int32_t* path, float* path_score, int32_t* path_idx) {
+    for (int t = threadIdx.x; t < B; t += blockDim.x) {
+        path[(size_t)b * B + t] = -1;
+        if (path_idx) path_idx[(size_t)b * B + t] = -1;
+    }
+    if (threadIdx.x == 0) path_score[b] = __int_as_float(0x7FC00000);
+}
+
 // The walk over precomputed transition scores, one workgroup per block.
 // Candidates, node scores and uniforms go to LDS first; T streams through a
 // double-buffered LDS ring, kWalkChunk floats (whole slots) per buffer, all
@@ -169,11 +178,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const int32_t* __res
     if (mode == 2)
         for (int t = tid; t < B; t += kWalkThreads) Us[t] = uniforms[(size_t)b * B + t];
     if (__syncthreads_or(bad)) {
-        for (int t = tid; t < B; t += kWalkThreads) {
-            path[(size_t)b * B + t] = -1;
-            if (path_idx) path_idx[(size_t)b * B + t] = -1;
-        }
-        if (tid == 0) path_score[b] = __int_as_float(0x7FC00000);
+        write_bad_block(b, B, path, path_score, path_idx);
         return;
     }
 
@@ -438,14 +443,6 @@ __device__ __forceinline__ void select_block_lds(int b, int a, const int32_t (*C
         if (path_idx) path_idx[(size_t)b * B] = -1;
         path_score[b] = mx;
     }
-}
-
-__device__ __forceinline__ void write_bad_block(int b, int B, int32_t* path, float* path_score, int32_t* path_idx) {
-    for (int t = threadIdx.x; t < B; t += blockDim.x) {
-        path[(size_t)b * B + t] = -1;
-        if (path_idx) path_idx[(size_t)b * B + t] = -1;
-    }
-    if (threadIdx.x == 0) path_score[b] = __int_as_float(0x7FC00000);
 }
 
 // Selector for bf16 tables with K <= 16, r % 32 == 0 and no gate, on given
