@@ -19,8 +19,8 @@ namespace {
 //    of KC channels (64 when D % 64 == 0, else 32).
 //  - Producer and consumer waves.  The NWB consumer waves split the 256
 //    vocabulary rows x 32 NWB hidden rows of a tile into blocks of NVB x
-//    (8 / NVB) accumulator tiles of 32x32 each; they only read LDS, issue
-//    MFMAs and store logits.  Four
+//    (8 / NVB) accumulator tiles of 32x32 each (8 x 1 at 256 rows, 4 x 2
+//    below); they only read LDS, issue MFMAs and store logits.  Four
 //    producer waves move the operands by direct global->LDS loads, two for W
 //    (a ring of RW stages) and two for the hidden rows (RY stages; L2
 //    resident, so a shallower ring).  A wave's count of outstanding memory
@@ -77,7 +77,12 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 #pragma clang diagnostic pop
 }
 
-constexpr bool kGemmStreamW = true;
+// The weight is read once, so its loads are non-temporal (they do not push
+// the reused hidden rows out of L2), except with 32-channel stages: there a
+// stage reads half of each 128-B weight line and the next stage the other
+// half, which has to find the line still in L2.
+template <int KC>
+constexpr bool kGemmStreamW = KC == 64;
 
 constexpr int kGemmProducers = 4;  // two W loaders, two hidden-row loaders
 
@@ -154,7 +159,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
                 const int vr = RPI * n + lane / UPR;
                 const int u = (lane % UPR) ^ gemm_swz<KC>(vr);
                 const int v = min(v0 + vr, v_end - 1);  // past the range: re-read its last row (cache hit)
-                dma16<kGemmStreamW>(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
+                dma16<kGemmStreamW<KC>>(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
             }
         };
         // Hidden-row load instructions of this producer per stage: with RS
@@ -201,6 +206,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
     // rows, and the NWB waves the 32 NWB hidden rows.  Per 16 channels a wave
     // reads NVB + NRB operand fragments from LDS for 8 MFMAs.
     constexpr int NRB = 8 / NVB, NVW = 8 / NVB;
+    static_assert(NVB * NRB == 8 && NWB % NVW == 0, "the consumer waves cover the 8 x NWB tiles of a stage");
     const int j = lane & 31, half = lane >> 5;
     const int vw = wave % NVW, rw = wave / NVW;
     // row blocks of this wave that hold rows (RS: the last row pass is
@@ -329,29 +335,31 @@ hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int n
     return hipGetLastError();
 }
 
-constexpr int kGemmNVB = 4;  // vocabulary blocks per consumer wave (x 2 row blocks)
 constexpr int kGemmSmallRows = 64;  // at most this many rows: 64-row passes (2 consumer waves)
 
 // More than 8 rows: one pass of the GEMM head per 256 rows instead of one
 // weight stream per 8 rows.
 bool use_gemm_head(const Dims& d) { return d.bf16 && d.rows() > kRowsPass; }
 
-template <int NWB, int KC, int RW, int RY>
+// NVB: vocabulary blocks per consumer wave.  8 x 1 blocks measured 5-7 %
+// faster than 4 x 2 with 8 consumer waves (256-row passes), and slower with
+// 2 or 4.
+template <int NWB, int KC, int RW, int RY, int NVB>
 hipError_t launch_head_gemm_rs(const Dims& d, const void* y, const void* W, int nch, float* logits, hipStream_t s) {
     // row skipping only where the last row pass is partial
-    return d.rows() % (32 * NWB) != 0 ? launch_head_gemm_t<NWB, KC, RW, RY, kGemmNVB, true>(d, y, W, nch, logits, s)
-                                      : launch_head_gemm_t<NWB, KC, RW, RY, kGemmNVB, false>(d, y, W, nch, logits, s);
+    return d.rows() % (32 * NWB) != 0 ? launch_head_gemm_t<NWB, KC, RW, RY, NVB, true>(d, y, W, nch, logits, s)
+                                      : launch_head_gemm_t<NWB, KC, RW, RY, NVB, false>(d, y, W, nch, logits, s);
 }
 
 hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {
     const int nch = head_chunks(d);
     if (d.D % 64 == 0) {
-        if (d.rows() <= kGemmSmallRows) return launch_head_gemm_rs<2, 64, 3, 2>(d, y, W, nch, logits, s);
-        return d.rows() <= 128 ? launch_head_gemm_rs<4, 64, 3, 2>(d, y, W, nch, logits, s)
-                               : launch_head_gemm_rs<8, 64, 3, 2>(d, y, W, nch, logits, s);
+        if (d.rows() <= kGemmSmallRows) return launch_head_gemm_rs<2, 64, 3, 2, 4>(d, y, W, nch, logits, s);
+        return d.rows() <= 128 ? launch_head_gemm_rs<4, 64, 3, 2, 4>(d, y, W, nch, logits, s)
+                               : launch_head_gemm_rs<8, 64, 3, 2, 8>(d, y, W, nch, logits, s);
     }
-    return d.rows() <= 128 ? launch_head_gemm_rs<4, 32, 6, 4>(d, y, W, nch, logits, s)
-                           : launch_head_gemm_rs<8, 32, 6, 4>(d, y, W, nch, logits, s);
+    return d.rows() <= 128 ? launch_head_gemm_rs<4, 32, 6, 4, 8>(d, y, W, nch, logits, s)
+                           : launch_head_gemm_rs<8, 32, 6, 4, 8>(d, y, W, nch, logits, s);
 }
 
 hipError_t launch_head_f32(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {

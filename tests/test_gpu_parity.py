@@ -149,6 +149,9 @@ HEAD_SHAPES = [
     S(batch=20, block=8, hidden=128, vocab=70000, top_k=64),
     S(batch=40, block=8, hidden=64, vocab=5000, top_k=5),
     S(batch=10, block=10, hidden=128, vocab=3001, top_k=16),  # 100 rows: a partial 128-row pass
+    S(batch=32, block=8, hidden=64, vocab=3001, top_k=16),    # one whole 256-row pass
+    S(batch=32, block=8, hidden=32, vocab=2000, top_k=8),     # 32-channel stages, whole 256-row pass
+    S(batch=20, block=8, hidden=96, vocab=9001, top_k=16),    # 32-channel stages, partial 256-row pass
 ]
 
 
