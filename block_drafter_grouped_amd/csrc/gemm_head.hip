@@ -1,7 +1,10 @@
 // Step 2 of the draft-block path for more than 8 rows (vLLM release-note
 // article on DFlash2, section "two additions": the target's lm_head and
 // log-softmax over the block's rows): the logits of every row as one GEMM,
-// and the fp32 head.  Both write fp32 logits; slice_topk.hip ranks them.
+// and the fp32 head.  Both write fp32 logits.  With K <= 16 the GEMM also
+// writes per-segment (max, sum of exp) partials and merge_seg_kernel below
+// ranks the few segments that can hold a row's top K; otherwise
+// slice_topk.hip ranks the logits.
 #include <algorithm>
 
 #include "common.h"
@@ -13,7 +16,7 @@ namespace {
 
 // Head for many rows (more than 8 per call, up to 256 per pass): a GEMM
 // logit[v][row] = <W[v], y[row]> on v_mfma_f32_32x32x16_bf16 that writes
-// the fp32 logits; the slice top-K kernel below ranks them.
+// the fp32 logits (and, MS, the segment partials described below).
 //  - One persistent workgroup per CU owns a contiguous vocabulary range and
 //    walks it in tiles of 256 rows of W against every hidden row, in stages
 //    of KC channels (64 when D % 64 == 0, else 32).
@@ -41,11 +44,15 @@ namespace {
 //  - Loads and MFMAs for rows past the work are skipped: weight rows past a
 //    CU's range in its last tile, and (RS) hidden rows past the last row in
 //    a partial row pass.
-// Ranking inside this kernel (a sorted per-lane list) was tried first: the
+// Ranking inside this kernel was tried twice.  A sorted per-lane list: the
 // lists of the 64 lanes of a wave take their insertions at different values,
 // so the wave ran nearly every insertion and the epilogue cost about a
-// quarter of the kernel.  Writing the logits costs a tenth of the weight
-// stream and the ranking then runs at the speed of reading them.
+// quarter of the kernel.  Appending the logits above a per-tile bound (the
+// smallest of the 16 lane-pair maxima of a row) as keys: the ballots and
+// scattered 8-B stores of every tile cost more than writing all the logits,
+// whose plain stores cost a tenth of the weight stream.  The kernel keeps
+// the stores and adds only the (max, sum of exp) of each segment, which
+// lets the merge read a few segments of the written logits per row.
 constexpr int kGemmTV = 256;
 
 template <int KC>
@@ -105,10 +112,38 @@ __device__ __forceinline__ void wait_vm(int n) {
     }
 }
 
-template <int NWB, int KC, int RW, int RY, int NVB, bool RS>
+// Segment partials (MS): besides the logits, every (row, segment) gets the
+// (max, sum of exp) of its logits.  A segment is the part of a tile one
+// consumer wave holds: the 32 NVB vocabulary entries of its blocks, for one
+// row (a row of a wave's tile is held by the 32 lanes of one half-wave, NVB
+// per lane).  The ranking kernel below combines the partials into the lse
+// and reads only the segments whose maximum can reach the row's top K.
+// Reductions over the 32 lanes of each half-wave; every lane receives its
+// half's result.  Four DPP steps reduce each 16-lane row; a swizzle that
+// swaps the two rows of a half (xor 16) combines them.
+__device__ __forceinline__ float swap_rows_of_half(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (16 << 10) | 0x1F));
+}
+__device__ __forceinline__ float max_of_half(float x) {
+    x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_f32<kDppMirror>(x));
+    return fmaxf(x, swap_rows_of_half(x));
+}
+// In a fixed order (the same on every run; the last add is commutative).
+__device__ __forceinline__ float sum_of_half(float x) {
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppHalfMirror>(x);
+    x += dpp_f32<kDppMirror>(x);
+    return x + swap_rows_of_half(x);
+}
+
+template <int NWB, int KC, int RW, int RY, int NVB, bool RS, bool MS>
 __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kernel(
     const uint16_t* __restrict__ y, int rows_total, int D, const uint16_t* __restrict__ W, int V, int nch,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, float2* __restrict__ cms, int nt) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int RP = 32 * NWB;
     constexpr int UPR = KC / 8;                 // 16-B units per LDS row
@@ -219,6 +254,19 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[vb][rb][r] = 0.f;
+    // MS: the wave's list (its vocabulary blocks of the chunk's range) and
+    // its segments, one per tile.
+    const int nseg = nch * NVW * nt;
+    const int list = c * NVW + vw;
+    if constexpr (MS) {
+        // segments of tiles past this list's range are empty
+        for (int tt = ntiles; tt < nt; ++tt) {
+            for (int i = lane; i < NRB * 32; i += kWave) {
+                const int row = row_base + rw * NRB * 32 + i;
+                if (row < rows_total) cms[(size_t)row * nseg + (size_t)list * nt + tt] = make_float2(-INFINITY, 0.f);
+            }
+        }
+    }
     int tile = 0, st = 0;
     for (int g = 0; g < total; ++g) {
         // vocabulary blocks of this wave that hold rows of the range (the
@@ -250,6 +298,49 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
             }
         }
         if (st == S - 1) {
+            if constexpr (MS) {
+                // Segment partials.  Register r of row block rb holds row
+                // 8 (r / 4) + 4 half + r % 4 of the block.  Entries past the
+                // range (the last tile of a list) read as -inf here; they are
+                // not stored either.
+                const int vt = v_beg + tile * kGemmTV;
+                const int seg = list * nt + tile;
+                if (nvb < NVB || vt + 32 * (vw * NVB + nvb) > v_end) {
+#pragma unroll
+                    for (int vb = 0; vb < NVB; ++vb) {
+                        const bool ok = vt + 32 * (vw * NVB + vb) + j < v_end;
+#pragma unroll
+                        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[vb][rb][r] = ok ? acc[vb][rb][r] : -INFINITY;
+                    }
+                }
+                // lanes 0 and 32 store the partials of their half's row
+                float2* const ms_lane = cms + (size_t)(4 * half) * nseg + seg;
+                const bool ms_writer = j == 0;
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    if (rb >= nrb) continue;  // wave-uniform: no rows in this block
+                    const int rowblk = row_base + (rw * NRB + rb) * 32;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row0 = rowblk + 8 * (r >> 2) + (r & 3);  // the row of half 0
+                        const int row = row0 + 4 * half;
+                        float lm = acc[0][rb][r];
+#pragma unroll
+                        for (int vb = 1; vb < NVB; ++vb) lm = fmaxf(lm, acc[vb][rb][r]);
+                        const float m = max_of_half(lm);
+                        float sl = 0.f;
+                        if (m > -INFINITY) {
+#pragma unroll
+                            for (int vb = 0; vb < NVB; ++vb) sl += __expf(acc[vb][rb][r] - m);
+                        }
+                        const float ssum = sum_of_half(sl);
+                        if (ms_writer && row < rows_total) ms_lane[(size_t)row0 * nseg] = make_float2(m, ssum);
+                        __builtin_amdgcn_sched_barrier(0);  // one row at a time: bounded registers
+                    }
+                }
+            }
             // Tile done.  For vocabulary block vb and row block rb the lane
             // holds logit[v][row] in acc[vb][rb][r], with v = the block's
             // vocabulary entry j and row = its row 8 (r / 4) + 4 half + r % 4.
@@ -319,19 +410,283 @@ __global__ __launch_bounds__(256) void head_f32_kernel(const float* __restrict__
     }
 }
 
+
+// Written logits + segment partials -> candidates (K <= 16).  One
+// workgroup of 1024 threads per row; wave w looks at segments w, w + 16, ...
+//  - lse = M + log S from the segments' (max, sum of exp), combined in a
+//    fixed order (lanes, then waves in order).
+//  - theta = the minimum over the 16 waves of the largest segment maximum a
+//    wave saw: 16 distinct logits of the row are >= theta, so every logit of
+//    the row's top K is >= theta.
+//  - Only segments whose maximum is >= theta can hold such a logit; for
+//    ordinary logits a few dozen of a row's segments.  They are listed in
+//    LDS, and theta is raised to the K-th largest of their maxima, which
+//    leaves about K segments.  The workgroup then reads their logits (one contiguous run of at
+//    most 256 per segment) with every thread holding several loads in
+//    flight, gathers the keys >= theta in LDS and places each by its rank
+//    among them (keys are distinct).  With more live segments than the list
+//    holds, each wave reads its own segments in turn instead.
+//  - If more than kSegGather keys pass (massively tied logits), the key
+//    threshold is raised to the exact K-th largest key by bisection,
+//    counting the keys >= the midpoint in the same segments; exactly K keys
+//    then pass.
+constexpr int kSegGather = 2048;
+constexpr int kSegLive = 2048;  // live segments listed in LDS
+constexpr int kSegUnroll = 16;  // logit loads in flight per thread
+constexpr int kSegRefine = 512; // at most this many live segments: tighter theta
+
+struct SegGeom {
+    int nch, nvw, nvb, nt, t32, V, span_log2;  // span: 32 nvb logits
+    // vocabulary run [beg, end) of segment sg (list sg / nt, tile sg % nt)
+    __device__ __forceinline__ void range(int sg, int& beg, int& end) const {
+        const int list = sg / nt, tile = sg - list * nt;
+        const int c = list / nvw, vw = list - c * nvw;
+        const int vb = (int)((int64_t)t32 * c / nch) * 32;
+        const int ve = min((int)((int64_t)t32 * (c + 1) / nch) * 32, V);
+        beg = vb + tile * kGemmTV + 32 * vw * nvb;
+        end = min(beg + 32 * nvb, ve);
+    }
+};
+
+__global__ __launch_bounds__(1024) void merge_seg_kernel(const float* __restrict__ logits,
+                                                         const float2* __restrict__ cms, SegGeom gm, int K,
+                                                         int32_t* __restrict__ cand_ids,
+                                                         float* __restrict__ cand_logp,
+                                                         float* __restrict__ lse_out) {
+    __shared__ uint64_t cand[kSegGather];
+    __shared__ int lbeg[kSegLive], lend[kSegLive];
+    __shared__ float lmax[kSegLive];
+    __shared__ int lbeg2[kSegRefine], lend2[kSegRefine];
+    __shared__ int nlive, nlive2;
+    __shared__ uint32_t th2_code;
+    __shared__ uint64_t fin[16];
+    __shared__ float2 wms[16];
+    __shared__ float gmax[16];
+    __shared__ uint64_t wtop[16];
+    __shared__ int wcnt[16];
+    __shared__ int cnt;
+    __shared__ float z_sh, th_sh;
+    __shared__ uint64_t top_sh;
+    const int row = blockIdx.x, t = threadIdx.x;
+    const int lane = t & (kWave - 1), wave = t / kWave;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    constexpr int NWV = 16;
+    const int nseg = gm.nch * gm.nvw * gm.nt;
+    const float2* ms = cms + (size_t)row * nseg;
+    const float* lrow = logits + (size_t)row * gm.V;
+    MaxSum x{-INFINITY, 0.f};
+    float g = -INFINITY;
+    float m_first = -INFINITY;  // maximum of this thread's first segment
+    for (int sg = wave + NWV * lane; sg < nseg; sg += NWV * kWave) {
+        const float2 p = ms[sg];
+        if (sg < NWV * kWave) m_first = p.x;
+        x = ms_combine(x, MaxSum{p.x, p.y});
+        g = fmaxf(g, p.x);
+    }
+    x = wave_ms_reduce(x);
+    g = wave_max_f32(g);
+    if (lane == 0) {
+        wms[wave] = make_float2(x.m, x.s);
+        gmax[wave] = g;
+    }
+    if (t == 0) {
+        cnt = 0;
+        nlive = 0;
+        nlive2 = 0;
+        th2_code = 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    if (wave == 0) {  // the 16 wave partials, combined in a fixed order
+        MaxSum zz{-INFINITY, 0.f};
+        float th = INFINITY;
+        if (lane < NWV) {
+            zz = MaxSum{wms[lane].x, wms[lane].y};
+            th = gmax[lane];
+        }
+        zz = wave_ms_reduce(zz);
+        th = -wave_max_f32(-th);
+        if (lane == 0) {
+            z_sh = (zz.m == -INFINITY) ? -INFINITY : zz.m + logf(zz.s);
+            th_sh = th;
+        }
+    }
+    __syncthreads();
+    float th = th_sh;
+    // The live segments (maximum >= th), listed in LDS; thread (w, l) looks
+    // at segments w + 16 (64 q + l), as above.
+    for (int q = 0; q * NWV * kWave < nseg; ++q) {
+        const int sg = wave + NWV * (kWave * q + lane);
+        const float msg = sg < nseg ? (q == 0 ? m_first : ms[sg].x) : -INFINITY;
+        const bool live = sg < nseg && msg >= th;
+        const uint64_t bal = __ballot(live);
+        if (bal == 0ull) continue;
+        int slot = 0;
+        if (lane == 0) slot = atomicAdd(&nlive, __popcll(bal));
+        slot = __shfl(slot, 0, kWave) + __popcll(bal & lt);
+        if (live && slot < kSegLive) {
+            int b0, e0;
+            gm.range(sg, b0, e0);
+            lbeg[slot] = b0;
+            lend[slot] = e0;
+            lmax[slot] = msg;
+        }
+    }
+    __syncthreads();
+    int nl = nlive;
+    const int* lb = lbeg;
+    const int* le = lend;
+    if (nl >= K && nl <= kSegRefine) {
+        // Tighter: th2 = the K-th largest maximum of the listed segments (the
+        // smallest one with fewer than K larger).  The maxima of K distinct
+        // segments are >= th2, so it bounds the row's K-th largest logit
+        // too, and only the segments whose maximum is >= th2 (K of them,
+        // ties aside) stay.  (With fewer than K listed segments there is no
+        // such bound.)
+        for (int i = t; i < nl; i += blockDim.x) {
+            const float mi = lmax[i];
+            int larger = 0;
+            for (int q = 0; q < nl; ++q) larger += lmax[q] > mi ? 1 : 0;
+            if (larger < K) atomicMin(&th2_code, (uint32_t)(make_key(mi, 0u) >> 32));
+        }
+        __syncthreads();
+        const uint32_t c2 = th2_code;
+        for (int i = t; i < nl; i += blockDim.x) {
+            if ((uint32_t)(make_key(lmax[i], 0u) >> 32) >= c2) {
+                const int slot = atomicAdd(&nlive2, 1);
+                lbeg2[slot] = lbeg[i];
+                lend2[slot] = lend[i];
+            }
+        }
+        __syncthreads();
+        nl = nlive2;
+        lb = lbeg2;
+        le = lend2;
+        th = key_value((uint64_t)c2 << 32);
+    }
+    // keys of logits >= th: the high word of a key orders the values
+    uint64_t theta = (uint64_t)(uint32_t)(make_key(th, 0u) >> 32) << 32;
+    // Calls f(key) for every logit of every live segment (all lanes call it;
+    // key 0 where a lane has no logit).
+    auto for_live = [&](auto&& f) {
+        if (nl <= kSegLive) {
+            const int total = nl << gm.span_log2;
+            const int smask = (1 << gm.span_log2) - 1;
+            for (int base = 0; base < total; base += 1024 * kSegUnroll) {
+                // All loads first (in-range addresses, no branches), so that
+                // they are in flight together; then the keys.
+                float val[kSegUnroll];
+                int vid[kSegUnroll];
+#pragma unroll
+                for (int u = 0; u < kSegUnroll; ++u) {
+                    const int i = min(base + 1024 * u + t, total - 1);
+                    const int ls = i >> gm.span_log2;
+                    const int v = lb[ls] + (i & smask);
+                    const bool ok = base + 1024 * u + t < total && v < le[ls];
+                    vid[u] = ok ? v : -1;
+                    val[u] = lrow[ok ? v : 0];
+                }
+#pragma unroll
+                for (int u = 0; u < kSegUnroll; ++u) f(vid[u] >= 0 ? make_key(val[u], (uint32_t)vid[u]) : 0ull);
+            }
+            return;
+        }
+        // Too many to list: lane l of wave w looks at segments w + 16 (64 q
+        // + l), and the wave reads the live ones in turn.
+        for (int q = 0; q * NWV * kWave < nseg; ++q) {
+            const int sg = wave + NWV * (kWave * q + lane);
+            const bool live = sg < nseg && ms[sg].x >= th;
+            uint64_t todo = __ballot(live);
+            while (todo) {
+                const int l = __ffsll((unsigned long long)todo) - 1;
+                todo &= todo - 1ull;
+                int beg, end;
+                gm.range(wave + NWV * (kWave * q + l), beg, end);
+                for (int v0 = beg; v0 < end; v0 += kWave) {
+                    const int v = v0 + lane;
+                    f(v < end ? make_key(lrow[v], (uint32_t)v) : 0ull);
+                }
+            }
+        }
+    };
+    // Pass 0 gathers the keys >= theta (and finds the row's largest key);
+    // if too many pass, bisection raises theta and pass 1 gathers again.
+    int n = 0;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        uint64_t top = 0ull;
+        for_live([&](uint64_t key) {
+            top = umax64(top, key);
+            const bool p = key >= theta && key != 0ull;
+            const uint64_t bal = __ballot(p);
+            if (bal == 0ull) return;
+            int slot = 0;
+            if (lane == 0) slot = atomicAdd(&cnt, __popcll(bal));
+            slot = __shfl(slot, 0, kWave) + __popcll(bal & lt);
+            if (p && slot < kSegGather) cand[slot] = key;
+        });
+        top = wave_max_u64(top);
+        if (lane == 0) wtop[wave] = top;
+        __syncthreads();
+        n = cnt;
+        if (n <= kSegGather) break;
+        if (t == 0) {
+            uint64_t tp = 0ull;
+            for (int w = 0; w < NWV; ++w) tp = umax64(tp, wtop[w]);
+            top_sh = tp;
+        }
+        __syncthreads();
+        // More than kSegGather >= K keys are >= theta, so the K-th largest
+        // lies in [theta, top].
+        uint64_t lo = theta, hi = top_sh;
+        while (lo < hi) {
+            const uint64_t mid = lo + (hi - lo) / 2 + 1;
+            int cc = 0;
+            for_live([&](uint64_t key) { cc += __popcll(__ballot(key >= mid)); });
+            if (lane == 0) wcnt[wave] = cc;
+            __syncthreads();
+            int all = 0;
+            for (int w = 0; w < NWV; ++w) all += wcnt[w];
+            __syncthreads();
+            if (all >= K) lo = mid;
+            else hi = mid - 1;
+        }
+        theta = lo;
+        __syncthreads();  // every thread has read cnt
+        if (t == 0) cnt = 0;
+        __syncthreads();
+    }
+    if (n > kSegGather) n = 0;  // unreachable: exactly K keys pass the exact threshold
+    __syncthreads();
+    for (int i = t; i < n; i += blockDim.x) {
+        const uint64_t key = cand[i];
+        int rank = 0;
+        for (int q = 0; q < n; ++q) rank += cand[q] > key ? 1 : 0;
+        if (rank < K) fin[rank] = key;
+    }
+    for (int i = n + t; i < K; i += blockDim.x) fin[i] = 0ull;
+    __syncthreads();
+    const float z = z_sh;
+    if (t < K) {
+        const uint64_t key = fin[t];
+        cand_ids[(size_t)row * K + t] = key_id(key);
+        cand_logp[(size_t)row * K + t] = key_value(key) - z;
+    }
+    if (t == 0) lse_out[row] = z;
+}
+
 }  // namespace
 
-template <int NWB, int KC, int RW, int RY, int NVB, bool RS>
-hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int nch, float* logits, hipStream_t s) {
+template <int NWB, int KC, int RW, int RY, int NVB, bool RS, bool MS>
+hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int nch, float* logits, float2* ms,
+                              int nt, hipStream_t s) {
     constexpr int RP = 32 * NWB;
     constexpr size_t lds = ((size_t)RW * kGemmTV + (size_t)RY * RP) * KC * 2;
     static_assert(lds <= 160 * 1024, "the stage rings must fit in LDS");
-    auto fn = head_gemm_kernel<NWB, KC, RW, RY, NVB, RS>;
+    auto fn = head_gemm_kernel<NWB, KC, RW, RY, NVB, RS, MS>;
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid(nch, (d.rows() + RP - 1) / RP);
     fn<<<grid, (NWB + kGemmProducers) * kWave, lds, s>>>((const uint16_t*)y, d.rows(), d.D, (const uint16_t*)W, d.V,
-                                                         nch, logits);
+                                                         nch, logits, ms, nt);
     return hipGetLastError();
 }
 
@@ -345,21 +700,59 @@ bool use_gemm_head(const Dims& d) { return d.bf16 && d.rows() > kRowsPass; }
 // faster than 4 x 2 with 8 consumer waves (256-row passes), and slower with
 // 2 or 4.
 template <int NWB, int KC, int RW, int RY, int NVB>
-hipError_t launch_head_gemm_rs(const Dims& d, const void* y, const void* W, int nch, float* logits, hipStream_t s) {
+hipError_t launch_head_gemm_rs(const Dims& d, const void* y, const void* W, int nch, float* logits, float2* ms,
+                               int nt, hipStream_t s) {
     // row skipping only where the last row pass is partial
-    return d.rows() % (32 * NWB) != 0 ? launch_head_gemm_t<NWB, KC, RW, RY, NVB, true>(d, y, W, nch, logits, s)
-                                      : launch_head_gemm_t<NWB, KC, RW, RY, NVB, false>(d, y, W, nch, logits, s);
+    const bool rs = d.rows() % (32 * NWB) != 0;
+    if (ms) {
+        return rs ? launch_head_gemm_t<NWB, KC, RW, RY, NVB, true, true>(d, y, W, nch, logits, ms, nt, s)
+                  : launch_head_gemm_t<NWB, KC, RW, RY, NVB, false, true>(d, y, W, nch, logits, ms, nt, s);
+    }
+    return rs ? launch_head_gemm_t<NWB, KC, RW, RY, NVB, true, false>(d, y, W, nch, logits, nullptr, 0, s)
+              : launch_head_gemm_t<NWB, KC, RW, RY, NVB, false, false>(d, y, W, nch, logits, nullptr, 0, s);
 }
 
-hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {
+// Vocabulary blocks per consumer wave of the configuration launch_head_gemm
+// picks (8: one wave spans the 256 tile rows; 4: two waves share them).
+static int gemm_nvb(const Dims& d) { return (d.D % 64 == 0 && d.rows() <= 128) ? 4 : 8; }
+
+GemmSegGeom gemm_seg_geom(const Dims& d) {
+    GemmSegGeom g{};
     const int nch = head_chunks(d);
+    const int64_t t32 = ((int64_t)d.V + 31) / 32;
+    const int64_t per = (t32 + nch - 1) / nch;  // most 32-row blocks of one chunk
+    g.nt = (int)((per + 7) / 8);
+    g.nvb = gemm_nvb(d);
+    g.nseg = nch * (8 / g.nvb) * g.nt;
+    return g;
+}
+
+static hipError_t head_gemm_dispatch(const Dims& d, const void* y, const void* W, float* logits, float2* ms,
+                                     hipStream_t s) {
+    const int nch = head_chunks(d);
+    const int nt = ms ? gemm_seg_geom(d).nt : 0;
     if (d.D % 64 == 0) {
-        if (d.rows() <= kGemmSmallRows) return launch_head_gemm_rs<2, 64, 3, 2, 4>(d, y, W, nch, logits, s);
-        return d.rows() <= 128 ? launch_head_gemm_rs<4, 64, 3, 2, 4>(d, y, W, nch, logits, s)
-                               : launch_head_gemm_rs<8, 64, 3, 2, 8>(d, y, W, nch, logits, s);
+        if (d.rows() <= kGemmSmallRows)
+            return launch_head_gemm_rs<2, 64, 3, 2, 4>(d, y, W, nch, logits, ms, nt, s);
+        return d.rows() <= 128 ? launch_head_gemm_rs<4, 64, 3, 2, 4>(d, y, W, nch, logits, ms, nt, s)
+                               : launch_head_gemm_rs<8, 64, 3, 2, 8>(d, y, W, nch, logits, ms, nt, s);
     }
-    return d.rows() <= 128 ? launch_head_gemm_rs<4, 32, 6, 4, 8>(d, y, W, nch, logits, s)
-                           : launch_head_gemm_rs<8, 32, 6, 4, 8>(d, y, W, nch, logits, s);
+    return d.rows() <= 128 ? launch_head_gemm_rs<4, 32, 6, 4, 8>(d, y, W, nch, logits, ms, nt, s)
+                           : launch_head_gemm_rs<8, 32, 6, 4, 8>(d, y, W, nch, logits, ms, nt, s);
+}
+
+hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, float2* seg_ms,
+                            hipStream_t s) {
+    return head_gemm_dispatch(d, y, W, logits, seg_ms, s);
+}
+
+hipError_t launch_merge_segs(const Dims& d, const float* logits, const float2* seg_ms, int32_t* cand_ids,
+                             float* cand_logp, float* lse, hipStream_t s) {
+    const GemmSegGeom g = gemm_seg_geom(d);
+    const int nch = head_chunks(d);
+    const SegGeom gm{nch, 8 / g.nvb, g.nvb, g.nt, (int)(((int64_t)d.V + 31) / 32), d.V, g.nvb == 8 ? 8 : 7};
+    merge_seg_kernel<<<d.rows(), 1024, 0, s>>>(logits, seg_ms, gm, d.K, cand_ids, cand_logp, lse);
+    return hipGetLastError();
 }
 
 hipError_t launch_head_f32(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s) {

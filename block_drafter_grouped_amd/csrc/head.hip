@@ -631,10 +631,13 @@ WsLayout ws_layout(const Dims& d) {
     };
     const size_t rows = (size_t)d.rows(), K = (size_t)d.K, nch = (size_t)head_chunks(d);
     const bool ranks_streaming = d.bf16 && d.K <= 16 && !use_gemm_head(d);
+    // the GEMM head writes segment partials that the segment merge reads
+    const bool ranks_segments = use_gemm_head(d) && d.K <= 16;
     L.y = take(rows * d.D * (d.bf16 ? 2 : 4));
-    L.keys = take(rows * nch * K * 8);
+    L.keys = take(rows * nch * K * 8);  // also what dfs_topk_logits ranks into
     L.ms = take(rows * nch * 8);
     L.logits = take(ranks_streaming ? 0 : rows * (size_t)d.V * 4);
+    L.segms = take(ranks_segments ? rows * gemm_seg_geom(d).nseg * 8 : 0);
     L.T = take((size_t)d.batch * (d.B - 1) * K * K * 4);
     L.cids = take(rows * K * 4);
     L.clogp = take(rows * K * 4);
@@ -658,7 +661,7 @@ hipError_t launch_head_partials(const Dims& d, const void* y, const void* W, flo
     float* logits = logits_f32 ? logits_f32 : (float*)(ws + L.logits);
     hipError_t e;
     if (use_gemm_head(d)) {
-        e = launch_head_gemm(d, y, W, logits, s);
+        e = launch_head_gemm(d, y, W, logits, nullptr, s);
     } else if (d.bf16) {
         // K > 16 on few rows: per-lane register lists of 64 keys would spill,
         // so the streaming kernel also writes the logits and the slice top-K
@@ -674,6 +677,14 @@ hipError_t launch_head_partials(const Dims& d, const void* y, const void* W, flo
 
 hipError_t launch_head_topk(const Dims& d, const void* y, const void* W, int32_t* cand_ids, float* cand_logp,
                             float* lse, float* logits_f32, char* ws, hipStream_t s) {
+    if (use_gemm_head(d) && d.K <= 16) {
+        const WsLayout L = ws_layout(d);
+        float* logits = logits_f32 ? logits_f32 : (float*)(ws + L.logits);
+        float2* segms = (float2*)(ws + L.segms);
+        hipError_t e = launch_head_gemm(d, y, W, logits, segms, s);
+        if (e != hipSuccess) return e;
+        return launch_merge_segs(d, logits, segms, cand_ids, cand_logp, lse, s);
+    }
     int nparts = 0;
     hipError_t e = launch_head_partials(d, y, W, logits_f32, ws, &nparts, s);
     if (e != hipSuccess) return e;

@@ -26,7 +26,7 @@ int head_chunks(const Dims& d);
 
 // Workspace carve-up (byte offsets from the 256-B aligned base).
 struct WsLayout {
-    size_t y, keys, ms, logits, T, cids, clogp, lse, zpart, total;
+    size_t y, keys, ms, logits, segms, T, cids, clogp, lse, zpart, total;
 };
 WsLayout ws_layout(const Dims& d);
 
@@ -56,8 +56,22 @@ hipError_t launch_head_partials(const Dims& d, const void* y, const void* W, flo
 // Heads that write fp32 logits [rows][V]: the GEMM head (bf16, more than
 // kRowsPass rows) and the fp32 head.
 bool use_gemm_head(const Dims& d);
-hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s);
+hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, float2* seg_ms,
+                            hipStream_t s);
 hipError_t launch_head_f32(const Dims& d, const void* y, const void* W, float* logits, hipStream_t s);
+
+// Segments of the GEMM head: a segment is the part of one tile that one
+// consumer wave holds, for one row (at most 256 consecutive logits of a
+// chunk's vocabulary range).  With seg_ms non-null the GEMM also writes the
+// (max, sum of exp) of every segment, layout [row][nseg].
+struct GemmSegGeom {
+    int nt, nvb, nseg;  // tiles per list, vocabulary blocks per wave, segments per row
+};
+GemmSegGeom gemm_seg_geom(const Dims& d);
+// Written logits + segment partials -> sorted candidates, log-probabilities
+// and lse (K <= 16).
+hipError_t launch_merge_segs(const Dims& d, const float* logits, const float2* seg_ms, int32_t* cand_ids,
+                             float* cand_logp, float* lse, hipStream_t s);
 
 // Per-slice top-K keys and (max, sum of exp) of written logits, in the
 // partial layout the merge reads ([row][k][slice], stride nsl).

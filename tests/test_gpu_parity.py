@@ -191,7 +191,13 @@ def check_head_fed(s, y_np, W_np, W_dev=None, rows=None):
             assert rel_err(lse[r], ref["lse"][0]) <= TOL
             assert not ids_match_or_explained(ids[r:r + 1], ref["ids"], lambda i: ref["logits"][0],
                                               tol_abs=TOL * 3.0)
-    # the timed mode (no logits written) returns the same candidates
+    check_timed_mode(s, y_np, W_np, W_dev, ids, lp, lse, logits)
+
+
+def check_timed_mode(s, y_np, W_np, W_dev, ids, lp, lse, logits):
+    """The timed mode (no logits written) returns the same candidates, score
+    and lse bits as the parity mode: both run the same kernels, only the
+    logits go to the workspace instead of the caller's buffer."""
     ids2, lp2, lse2, _ = run_head(s, y_np, W_np, W_dev, with_logits=False)
     assert np.array_equal(ids2, ids) and np.array_equal(lp2, lp) and np.array_equal(lse2, lse)
 
@@ -228,7 +234,9 @@ def test_head_topk_fed_full_size(cfg_id):
 
 @pytest.mark.parametrize("s", [
     S(block=8, hidden=256, vocab=5000, top_k=16),              # streaming head
-    S(batch=2, block=8, hidden=256, vocab=5000, top_k=16),     # GEMM head + slice top-K
+    S(batch=2, block=8, hidden=256, vocab=5000, top_k=16),     # GEMM head: slice top-K, rank epilogue
+    S(batch=5, block=8, hidden=128, vocab=5003, top_k=4),      # rank epilogue, two waves per tile row
+    S(batch=32, block=8, hidden=128, vocab=5000, top_k=16),    # rank epilogue, a whole 256-row pass
     S(block=8, hidden=256, vocab=3000, top_k=40),              # K > 16
 ], ids=str)
 @pytest.mark.parametrize("kind", ["zero_rows", "duplicate_weights"])
@@ -246,6 +254,7 @@ def test_head_topk_massive_ties(s, kind):
     ids, lp, lse, logits = run_head(s, y, W)
     rid, rlse = topk_of(logits, s.top_k)
     assert np.array_equal(ids, rid)
+    check_timed_mode(s, y, W, None, ids, lp, lse, logits)
     ref = orc.head(s, y, W, want_logits=True)
     assert np.array_equal(ids, ref["ids"])
     assert rel_err(lse, ref["lse"]) <= 1e-5
