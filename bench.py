@@ -308,7 +308,9 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic_gbs,
                 "traffic_unit": "GB/s", "traffic_bytes_per_launch": traffic,
-                "kernel": "lm_head + top-K stage (head_gemm_kernel + slice_topk_kernel + merge16_kernel, "
+                "kernel": "lm_head + top-K stage (head_gemm_kernel with segment partials + merge_seg_kernel, "
+                          "one dfs_head_topk call)" if s.top_k <= 16 else
+                          "lm_head + top-K stage (head_gemm_kernel + slice_topk_kernel + merge64_kernel, "
                           "one dfs_head_topk call)",
                 "flops_per_launch": fl, "bytes_per_launch": hb, "us_per_launch": round(us_head, 2)}
     else:
