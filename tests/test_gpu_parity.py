@@ -152,6 +152,7 @@ HEAD_SHAPES = [
     S(batch=32, block=8, hidden=64, vocab=3001, top_k=16),    # one whole 256-row pass
     S(batch=32, block=8, hidden=32, vocab=2000, top_k=8),     # 32-channel stages, whole 256-row pass
     S(batch=20, block=8, hidden=96, vocab=9001, top_k=16),    # 32-channel stages, partial 256-row pass
+    S(batch=40, block=8, hidden=128, vocab=70001, top_k=16),  # two row passes, segment merge
 ]
 
 
@@ -214,6 +215,9 @@ def test_head_topk_fed(s):
 # 128 stages per tile).  Checked against the oracle on sampled rows.
 MAX_HEAD_SHAPES = [
     S(block=4, hidden=64, vocab=1 << 21, top_k=64),
+    # the GEMM head's segment merge at the largest vocabulary: 32 tiles per
+    # list, 16 384 segments per row
+    S(batch=3, block=8, hidden=64, vocab=1 << 21, top_k=16),
     S(block=8, hidden=8192, vocab=20000, top_k=16),
     S(batch=3, block=8, hidden=8192, vocab=20000, top_k=16),
 ]
