@@ -3,9 +3,11 @@
 // release-note article on DFlash2, section "two additions": keep the target
 // head's top-K per slot).  Up to 8 rows with K <= 16 (the batch-1 case) the
 // logits are never written to HBM: the streaming head keeps, per vocabulary
-// chunk, each row's top-K keys and its (max, sum of exp) pair.  Otherwise a
-// head that writes the logits (gemm_head.hip) is followed by the slice top-K
-// (slice_topk.hip).  A merge kernel here combines the chunk partials.
+// chunk, each row's top-K keys and its (max, sum of exp) pair.  More rows
+// with K <= 16: the GEMM head writes the logits and per-segment partials,
+// and its segment merge ranks them (gemm_head.hip).  Otherwise a head that
+// writes the logits is followed by the slice top-K (slice_topk.hip).  The
+// merge kernels here combine chunk or slice partials.
 //
 // bf16 streaming head (up to 8 rows): the work is a stream of the [V, D]
 // weight (2.5 GB at D 5120, V 248 320) against a tiny [rows, D] operand, so

@@ -41,9 +41,9 @@ size_t conv_ws_bytes(const Dims& d);
 hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32, char* ws,
                        hipStream_t s, int layers = 1);
 
-// Head + top-K.  Uses ws.keys / ws.ms, and ws.logits when the logits are
-// ranked after the head (fp32, K > 16, more than 8 rows) and logits_f32 is
-// NULL.
+// Head + top-K.  Uses ws.keys / ws.ms; ws.logits when the logits are
+// written (fp32, K > 16, more than 8 rows) and logits_f32 is NULL; and
+// ws.segms for the GEMM head's segment partials (more than 8 rows, K <= 16).
 hipError_t launch_head_topk(const Dims& d, const void* y, const void* W, int32_t* cand_ids,
                             float* cand_logp, float* lse, float* logits_f32, char* ws,
                             hipStream_t s);

@@ -155,8 +155,13 @@ size_t dfs_conv_layers_workspace_size(const dfs_config* cfg, int32_t layers);
  *  logits_f32 [rows, V]  fp32, optional (NULL): also writes every logit (the
  *                        exact values the top-K was taken from), for parity
  *  ws, ws_bytes          workspace (see conventions)
- * The logits are never materialised otherwise: each workgroup keeps its own
- * top-K and (max, sum of exp) partials, merged by a second kernel.
+ * Up to 8 rows (bf16, K <= 16) the logits are never materialised otherwise:
+ * each workgroup keeps its own top-K and (max, sum of exp) partials, merged
+ * by a second kernel.  With more rows the logits go to the workspace (or to
+ * logits_f32) together with the (max, sum of exp) of every 256-logit
+ * segment, and the merge reads only the segments that can hold a row's top
+ * K (K <= 16) or ranks every slice of the logits (K > 16).  Both modes give
+ * the same bits.
  */
 int dfs_head_topk(const dfs_config* cfg, const void* y, const void* W,
                   int32_t* cand_ids, float* cand_logp, float* lse,
