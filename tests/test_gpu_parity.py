@@ -238,9 +238,11 @@ def test_head_topk_fed_full_size(cfg_id):
 
 @pytest.mark.parametrize("s", [
     S(block=8, hidden=256, vocab=5000, top_k=16),              # streaming head
-    S(batch=2, block=8, hidden=256, vocab=5000, top_k=16),     # GEMM head: slice top-K, rank epilogue
-    S(batch=5, block=8, hidden=128, vocab=5003, top_k=4),      # rank epilogue, two waves per tile row
-    S(batch=32, block=8, hidden=128, vocab=5000, top_k=16),    # rank epilogue, a whole 256-row pass
+    S(batch=2, block=8, hidden=256, vocab=5000, top_k=16),     # GEMM head, segment merge
+    S(batch=5, block=8, hidden=128, vocab=5003, top_k=4),      # segment merge, two waves per tile row
+    S(batch=32, block=8, hidden=128, vocab=5000, top_k=16),    # segment merge, a whole 256-row pass
+    # 8192 segments per row, all live: more than the merge lists in LDS
+    S(batch=2, block=8, hidden=64, vocab=1 << 20, top_k=16),
     S(block=8, hidden=256, vocab=3000, top_k=40),              # K > 16
 ], ids=str)
 @pytest.mark.parametrize("kind", ["zero_rows", "duplicate_weights"])
