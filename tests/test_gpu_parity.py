@@ -854,6 +854,25 @@ def test_draft_block_deterministic_and_stream():
         assert np.array_equal(x, y, equal_nan=True)
 
 
+@pytest.mark.parametrize("s", [
+    S(batch=32, block=8, hidden=256, vocab=30011, top_k=16),   # GEMM head, segment merge
+    S(batch=6, block=8, hidden=128, vocab=30011, top_k=40),    # GEMM head, slice top-K
+], ids=str)
+def test_draft_block_deterministic_many_rows(s):
+    """The many-row paths give the same bits on every call and on another
+    stream: the segment partials and merges combine in a fixed order."""
+    inp = wl.make_inputs_for(s, 29)
+    dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
+    dev["wg_cm"] = to_dev(wg_channel_major(inp["wg"]))
+    a = run_block(s, dev)
+    b = run_block(s, dev)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        c = run_block(s, dev, stream=st)
+    for x, y, z in zip(a, b, c):
+        assert np.array_equal(x, y, equal_nan=True) and np.array_equal(x, z, equal_nan=True)
+
+
 def test_draft_block_long_block_planted():
     """Long-block workload (batch 8, B 16) with transition plants: paths
     against the oracle reference in tests/golden/plant_w4.json (written by
