@@ -416,16 +416,17 @@ __global__ __launch_bounds__(256) void head_f32_kernel(const float* __restrict__
 //  - lse = M + log S from the segments' (max, sum of exp), combined in a
 //    fixed order (lanes, then waves in order).
 //  - theta = the minimum over the 16 waves of the largest segment maximum a
-//    wave saw: 16 distinct logits of the row are >= theta, so every logit of
-//    the row's top K is >= theta.
+//    wave saw (-inf if a wave saw no logit): 16 distinct logits of the row
+//    are >= theta, so every logit of the row's top K is >= theta.
 //  - Only segments whose maximum is >= theta can hold such a logit; for
 //    ordinary logits a few dozen of a row's segments.  They are listed in
 //    LDS, and theta is raised to the K-th largest of their maxima, which
-//    leaves about K segments.  The workgroup then reads their logits (one contiguous run of at
-//    most 256 per segment) with every thread holding several loads in
-//    flight, gathers the keys >= theta in LDS and places each by its rank
-//    among them (keys are distinct).  With more live segments than the list
-//    holds, each wave reads its own segments in turn instead.
+//    leaves about K segments.  The workgroup then reads their logits (one
+//    contiguous run of at most 256 per segment) with every thread holding
+//    several loads in flight, gathers the keys >= theta in LDS and places
+//    each by its rank among them (keys are distinct).  With more live
+//    segments than the list holds, each wave reads its own segments in turn
+//    instead.
 //  - If more than kSegGather keys pass (massively tied logits), the key
 //    threshold is raised to the exact K-th largest key by bisection,
 //    counting the keys >= the midpoint in the same segments; exactly K keys
