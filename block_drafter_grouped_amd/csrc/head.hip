@@ -357,12 +357,8 @@ __global__ __launch_bounds__(1024) void merge16_kernel(const uint64_t* __restric
     __syncthreads();
     const uint64_t theta = theta_sh;
     bool pass[4];
-    int mine = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        pass[e] = k4[e] >= theta && k4[e] != 0ull;
-        mine += pass[e] ? 1 : 0;
-    }
+    for (int e = 0; e < 4; ++e) pass[e] = k4[e] >= theta && k4[e] != 0ull;
     // Slots: wave-aggregated offsets from ballots, one LDS atomic per wave.
     const uint64_t lt = (1ull << lane) - 1ull;
     int before = 0, total = 0;
