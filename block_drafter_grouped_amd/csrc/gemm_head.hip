@@ -546,14 +546,21 @@ __global__ __launch_bounds__(1024) void merge_seg_kernel(const float* __restrict
         for (int i = t; i < nl; i += blockDim.x) {
             const float mi = lmax[i];
             int larger = 0;
+#pragma unroll 8
             for (int q = 0; q < nl; ++q) larger += lmax[q] > mi ? 1 : 0;
             if (larger < K) atomicMin(&th2_code, (uint32_t)(make_key(mi, 0u) >> 32));
         }
         __syncthreads();
         const uint32_t c2 = th2_code;
-        for (int i = t; i < nl; i += blockDim.x) {
-            if ((uint32_t)(make_key(lmax[i], 0u) >> 32) >= c2) {
-                const int slot = atomicAdd(&nlive2, 1);
+        for (int i0 = 0; i0 < nl; i0 += blockDim.x) {  // wave-aggregated slots
+            const int i = i0 + t;
+            const bool keep = i < nl && (uint32_t)(make_key(lmax[i], 0u) >> 32) >= c2;
+            const uint64_t bal = __ballot(keep);
+            if (bal == 0ull) continue;
+            int slot = 0;
+            if (lane == 0) slot = atomicAdd(&nlive2, __popcll(bal));
+            slot = __shfl(slot, 0, kWave) + __popcll(bal & lt);
+            if (keep) {
                 lbeg2[slot] = lbeg[i];
                 lend2[slot] = lend[i];
             }
@@ -574,20 +581,25 @@ __global__ __launch_bounds__(1024) void merge_seg_kernel(const float* __restrict
             const int smask = (1 << gm.span_log2) - 1;
             for (int base = 0; base < total; base += 1024 * kSegUnroll) {
                 // All loads first (in-range addresses, no branches), so that
-                // they are in flight together; then the keys.
-                float val[kSegUnroll];
-                int vid[kSegUnroll];
+                // they are in flight together; then the keys.  Only as many
+                // groups of 4 loads as the live logits need.
+                const int groups = min(kSegUnroll / 4, (total - base + 4095) / 4096);
+                for (int gq = 0; gq < groups; ++gq) {
+                    float val[4];
+                    int vid[4];
 #pragma unroll
-                for (int u = 0; u < kSegUnroll; ++u) {
-                    const int i = min(base + 1024 * u + t, total - 1);
-                    const int ls = i >> gm.span_log2;
-                    const int v = lb[ls] + (i & smask);
-                    const bool ok = base + 1024 * u + t < total && v < le[ls];
-                    vid[u] = ok ? v : -1;
-                    val[u] = lrow[ok ? v : 0];
+                    for (int u = 0; u < 4; ++u) {
+                        const int iu = base + 1024 * (4 * gq + u) + t;
+                        const int i = min(iu, total - 1);
+                        const int ls = i >> gm.span_log2;
+                        const int v = lb[ls] + (i & smask);
+                        const bool ok = iu < total && v < le[ls];
+                        vid[u] = ok ? v : -1;
+                        val[u] = lrow[ok ? v : 0];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) f(vid[u] >= 0 ? make_key(val[u], (uint32_t)vid[u]) : 0ull);
                 }
-#pragma unroll
-                for (int u = 0; u < kSegUnroll; ++u) f(vid[u] >= 0 ? make_key(val[u], (uint32_t)vid[u]) : 0ull);
             }
             return;
         }
@@ -660,6 +672,7 @@ __global__ __launch_bounds__(1024) void merge_seg_kernel(const float* __restrict
     for (int i = t; i < n; i += blockDim.x) {
         const uint64_t key = cand[i];
         int rank = 0;
+#pragma unroll 8
         for (int q = 0; q < n; ++q) rank += cand[q] > key ? 1 : 0;
         if (rank < K) fin[rank] = key;
     }
