@@ -19,7 +19,7 @@ ARCH = os.environ.get("DFS_OFFLOAD_ARCH", "gfx950")
 # library binds to that runtime (see dflash2.py).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
+         "-fvisibility=hidden", "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 
 
 def _compile(src: str, verbose: bool) -> str:

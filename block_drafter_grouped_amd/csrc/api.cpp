@@ -1,10 +1,11 @@
 // C ABI of libdflash2: argument validation on the host, then kernel launches
-// on the caller's stream.  No allocation, no synchronisation, no state.
+// on the caller's stream.  No allocation and no synchronisation.
 #include <stdint.h>
 
 #include <cmath>
 
 #include "../../include/dflash2.h"
+#include "api_internal.h"
 #include "kernels.h"
 
 namespace {
@@ -55,6 +56,21 @@ int check_ws(const dfs_config* c, const void* ws, size_t ws_bytes) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DFS_OK : DFS_ERR_HIP; }
+
+// Selector options: NULL means the best-path walk without a gate.
+int check_opts(const dfs_select_opts* o, dfs::SelectOpts* out) {
+    *out = dfs::SelectOpts{nullptr, DFS_WALK_VITERBI, 1.f, nullptr};
+    if (!o) return DFS_OK;
+    if (o->walk != DFS_WALK_VITERBI && o->walk != DFS_WALK_GREEDY && o->walk != DFS_WALK_SAMPLE)
+        return DFS_ERR_UNSUPPORTED;
+    if (o->walk == DFS_WALK_SAMPLE) {
+        if (!o->uniforms) return DFS_ERR_NULL;
+        if (!(o->temperature > 0.f) || !std::isfinite(o->temperature)) return DFS_ERR_SHAPE;
+    }
+    if (misaligned(o->gate, 16) || misaligned(o->uniforms, 16)) return DFS_ERR_MISALIGNED;
+    *out = dfs::SelectOpts{o->gate, o->walk, o->temperature, o->walk == DFS_WALK_SAMPLE ? o->uniforms : nullptr};
+    return DFS_OK;
+}
 
 }  // namespace
 
@@ -137,21 +153,6 @@ int dfs_topk_logits(const dfs_config* cfg, const float* logits, int32_t* cand_id
         dfs::launch_topk_logits(dims_of(cfg), logits, cand_ids, cand_logp, lse, (char*)ws, (hipStream_t)stream));
 }
 
-// Selector options: NULL means the best-path walk without a gate.
-int check_opts(const dfs_select_opts* o, dfs::SelectOpts* out) {
-    *out = dfs::SelectOpts{nullptr, DFS_WALK_VITERBI, 1.f, nullptr};
-    if (!o) return DFS_OK;
-    if (o->walk != DFS_WALK_VITERBI && o->walk != DFS_WALK_GREEDY && o->walk != DFS_WALK_SAMPLE)
-        return DFS_ERR_UNSUPPORTED;
-    if (o->walk == DFS_WALK_SAMPLE) {
-        if (!o->uniforms) return DFS_ERR_NULL;
-        if (!(o->temperature > 0.f) || !std::isfinite(o->temperature)) return DFS_ERR_SHAPE;
-    }
-    if (misaligned(o->gate, 16) || misaligned(o->uniforms, 16)) return DFS_ERR_MISALIGNED;
-    *out = dfs::SelectOpts{o->gate, o->walk, o->temperature, o->walk == DFS_WALK_SAMPLE ? o->uniforms : nullptr};
-    return DFS_OK;
-}
-
 int dfs_select(const dfs_config* cfg, const dfs_select_opts* opts, const int32_t* anchor, const int32_t* cand_ids,
                const float* cand_logp, const void* P, const void* Q, int32_t* path, float* path_score,
                int32_t* path_idx, void* ws, size_t ws_bytes, void* stream) {
@@ -171,6 +172,21 @@ int dfs_select(const dfs_config* cfg, const dfs_select_opts* opts, const int32_t
 int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts, const void* h, const int32_t* anchor,
                     const void* wg_cm, const void* W, const void* P, const void* Q, int32_t* path, float* path_score,
                     int32_t* cand_ids, float* cand_logp, void* ws, size_t ws_bytes, void* stream) {
+    dfs::SelectOpts o;
+    int st = dfs::check_draft_block(cfg, opts, h, anchor, wg_cm, W, P, Q, path, path_score, cand_ids, cand_logp, &o);
+    if (st) return st;
+    if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+    return dfs::launch_draft_block(cfg, o, h, anchor, wg_cm, W, P, Q, path, path_score, cand_ids, cand_logp,
+                                   (char*)ws, stream);
+}
+
+}  // extern "C"
+
+namespace dfs {
+
+int check_draft_block(const dfs_config* cfg, const dfs_select_opts* opts, const void* h, const int32_t* anchor,
+                      const void* wg_cm, const void* W, const void* P, const void* Q, int32_t* path,
+                      float* path_score, int32_t* cand_ids, float* cand_logp, SelectOpts* o) {
     int st = check_cfg(cfg);
     if (st) return st;
     if (!h || !anchor || !wg_cm || !W || !P || !Q || !path || !path_score) return DFS_ERR_NULL;
@@ -178,21 +194,24 @@ int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts, const vo
         misaligned(P, 16) || misaligned(Q, 16) || misaligned(path, 16) || misaligned(path_score, 16) ||
         misaligned(cand_ids, 16) || misaligned(cand_logp, 16))
         return DFS_ERR_MISALIGNED;
-    dfs::SelectOpts o;
-    if ((st = check_opts(opts, &o))) return st;
-    if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+    return check_opts(opts, o);
+}
+
+int launch_draft_block(const dfs_config* cfg, const SelectOpts& o, const void* h, const int32_t* anchor,
+                       const void* wg_cm, const void* W, const void* P, const void* Q, int32_t* path,
+                       float* path_score, int32_t* cand_ids, float* cand_logp, char* w, void* stream) {
     const Dims d = dims_of(cfg);
-    const dfs::WsLayout L = dfs::ws_layout(d);
-    char* w = (char*)ws;
+    const WsLayout L = ws_layout(d);
     hipStream_t s = (hipStream_t)stream;
+    int st;
     // One tap: the conv is the identity, so the head reads h directly.
     const void* y = d.ks == 1 ? h : (const void*)(w + L.y);
     int32_t* cids = cand_ids ? cand_ids : (int32_t*)(w + L.cids);
     float* clogp = cand_logp ? cand_logp : (float*)(w + L.clogp);
     float* lse = (float*)(w + L.lse);
-    if (d.ks != 1 && (st = hip_status(dfs::launch_conv(d, h, wg_cm, w + L.y, nullptr, w, s)))) return st;
-    if ((st = hip_status(dfs::launch_head_topk(d, y, W, cids, clogp, lse, nullptr, w, s)))) return st;
-    return hip_status(dfs::launch_select(d, o, anchor, cids, clogp, P, Q, path, path_score, nullptr, w, s));
+    if (d.ks != 1 && (st = hip_status(launch_conv(d, h, wg_cm, w + L.y, nullptr, w, s)))) return st;
+    if ((st = hip_status(launch_head_topk(d, y, W, cids, clogp, lse, nullptr, w, s)))) return st;
+    return hip_status(launch_select(d, o, anchor, cids, clogp, P, Q, path, path_score, nullptr, w, s));
 }
 
-}  // extern "C"
+}  // namespace dfs

@@ -696,7 +696,8 @@ hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int n
     constexpr size_t lds = ((size_t)RW * kGemmTV + (size_t)RY * RP) * KC * 2;
     static_assert(lds <= 160 * 1024, "the stage rings must fit in LDS");
     auto fn = head_gemm_kernel<NWB, KC, RW, RY, NVB, RS, MS>;
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static LdsAttr attr;
+    hipError_t e = ensure_lds(attr, (const void*)fn, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid(nch, (d.rows() + RP - 1) / RP);
     fn<<<grid, (NWB + kGemmProducers) * kWave, lds, s>>>((const uint16_t*)y, d.rows(), d.D, (const uint16_t*)W, d.V,

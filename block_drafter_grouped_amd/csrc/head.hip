@@ -1,9 +1,10 @@
 // Steps 2-3 of the draft-block path: the vocabulary head (the target's
 // shared lm_head), log-softmax and the per-slot top-K candidates (vLLM
-// release-note article on DFlash2, section "two additions": keep the target
-// head's top-K per slot).  Up to 8 rows with K <= 16 (the batch-1 case) the
-// logits are never written to HBM: the streaming head keeps, per vocabulary
-// chunk, each row's top-K keys and its (max, sum of exp) pair.  More rows
+// release-note article on DFlash2, section "two additions": at each slot the
+// selector works on the K tokens the target head ranks highest).  Up to 8
+// rows with K <= 16 (the batch-1 case) the logits are never written to HBM:
+// the streaming head keeps, per vocabulary chunk, each row's top-K keys and
+// its (max, sum of exp) pair.  More rows
 // with K <= 16: the GEMM head writes the logits and per-segment partials,
 // and its segment merge ranks them (gemm_head.hip).  Otherwise a head that
 // writes the logits is followed by the slice top-K (slice_topk.hip).  The
@@ -554,7 +555,8 @@ hipError_t launch_head_bf16_t(const Dims& d, int K, const void* y, const void* W
     const size_t merge = (size_t)kRowsPass * NW * 4 * K * 8 + (size_t)kRowsPass * NW * 4 * 8;
     lds = std::max(std::max(lds, merge), kMinHeadLds);
     auto fn = head_bf16_kernel<NW, U, KL>;
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static LdsAttr attr;
+    hipError_t e = ensure_lds(attr, (const void*)fn, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid(nch, (d.rows() + kRowsPass - 1) / kRowsPass);
     fn<<<grid, NW * kWave, lds, s>>>((const uint16_t*)y, d.rows(), d.D, (const uint16_t*)W, d.V, nch, K, keys, ms,
@@ -581,7 +583,8 @@ hipError_t launch_head_pair_t(const Dims& d, int K, const void* y, const void* W
     const size_t merge = (size_t)kRowsPass * NW * 2 * K * 8 + (size_t)kRowsPass * NW * 2 * 8;
     lds = std::max(std::max(lds, merge), kMinHeadLds);
     auto fn = head_pair_kernel<NW, U>;
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static LdsAttr attr;
+    hipError_t e = ensure_lds(attr, (const void*)fn, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid(nch, (d.rows() + kRowsPass - 1) / kRowsPass);
     fn<<<grid, NW * kWave, lds, s>>>((const uint16_t*)y, d.rows(), d.D, (const uint16_t*)W, d.V, nch, K, keys, ms,

@@ -7,7 +7,30 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace dfs {
+
+// The dynamic-LDS limit a kernel was raised to, per device.  A launcher keeps
+// one static instance per kernel; ensure_lds() calls hipFuncSetAttribute only
+// when a launch needs more LDS than any earlier launch of that kernel on the
+// current device, so steady-state calls make no attribute call.
+constexpr int kLdsAttrDevices = 64;
+struct LdsAttr {
+    std::atomic<int> bytes[kLdsAttrDevices];
+};
+inline hipError_t ensure_lds(LdsAttr& a, const void* fn, int bytes) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kLdsAttrDevices)
+        return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    int have = a.bytes[dev].load(std::memory_order_acquire);
+    if (have >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    while (have < bytes && !a.bytes[dev].compare_exchange_weak(have, bytes, std::memory_order_acq_rel)) {
+    }
+    return hipSuccess;
+}
 
 struct Dims {
     int batch, B, D, V, K, r, gs, ks;

@@ -488,8 +488,8 @@ hipError_t launch_select(const Dims& d, const SelectOpts& o, const int32_t* anch
     // best path at every length measured (up to 64).
     if (!o.gate && d.bf16 && d.K <= 16 && d.r % 32 == 0 && (o.walk == 0 || d.B <= 16)) {
         const size_t lds = (size_t)(d.B - 1) * 16 * 16 * sizeof(float);
-        hipError_t e = hipFuncSetAttribute((const void*)select_fused_kernel<8>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        static LdsAttr attr;
+        hipError_t e = ensure_lds(attr, (const void*)select_fused_kernel<8>, (int)lds);
         if (e != hipSuccess) return e;
         select_fused_kernel<8><<<d.batch, 8 * kWave, lds, s>>>(anchor, cand_ids, cand_logp, (const uint16_t*)P,
                                                              (const uint16_t*)Q, o.walk, o.temperature, o.uniforms,

@@ -8,9 +8,15 @@
  *
  *   1. grouped dynamic depthwise causal conv inside the block
  *      (vLLM release-note article on DFlash2, section "two additions");
- *   2. vocabulary head (the target's lm_head) with log-softmax, over all rows;
- *   3. per-slot top-K candidates over the full vocabulary
- *      (same section: "keep the target head's top-K per slot");
+ *   2. vocabulary head (the target's lm_head) with log-softmax, over all rows
+ *      (same section: the selector's candidates are ranked by the target
+ *      model's head; Inco AI post "DFlash 2: keep the draft parallel",
+ *      section "lightweight path selector": a candidate's node score is the
+ *      drafter's own logit, taken here as its log-probability);
+ *   3. per-slot top-K candidates over the full vocabulary (same section of
+ *      the release-note article: rather than one argmax per draft slot, the
+ *      selector retains the K tokens the target head ranks highest at every
+ *      slot);
  *   4. low-rank adjacent-transition scores <P[a], Q[b]> between the
  *      candidates of neighbouring slots (Inco AI post "DFlash 2: keep the
  *      draft parallel", section "lightweight path selector", with the
@@ -37,7 +43,8 @@
  *    is done.  The caller synchronises before reading outputs.
  *  - Ownership: the caller owns every buffer, including the workspace
  *    (>= dfs_workspace_size(cfg) bytes; contents undefined between calls;
- *    one call at a time per workspace).  The library keeps no state.
+ *    one call at a time per workspace).  The library keeps no state besides
+ *    the kernels' LDS attributes (set once per process).
  *  - Errors: the return value is a dfs_status.  All argument checks happen on
  *    the host BEFORE any HIP call, so a rejected call touches no device
  *    state.  DFS_ERR_HIP reports a failed kernel launch; faults inside a
@@ -53,6 +60,13 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* Only the declarations below are exported from the shared library. */
+#if defined(__GNUC__) || defined(__clang__)
+#define DFS_API __attribute__((visibility("default")))
+#else
+#define DFS_API
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -84,13 +98,13 @@ typedef struct {
 } dfs_config;
 
 /* Bytes of workspace any entry point needs for `cfg` (0 if cfg is invalid). */
-size_t dfs_workspace_size(const dfs_config* cfg);
+DFS_API size_t dfs_workspace_size(const dfs_config* cfg);
 
 /* Static description of a status code (never NULL). */
-const char* dfs_status_string(int status);
+DFS_API const char* dfs_status_string(int status);
 
 /* Checks `cfg` alone (no pointers).  DFS_OK or the first violated rule. */
-int dfs_validate_config(const dfs_config* cfg);
+DFS_API int dfs_validate_config(const dfs_config* cfg);
 
 /*
  * Step 1: grouped dynamic depthwise causal conv (release-note article,
@@ -115,7 +129,7 @@ int dfs_validate_config(const dfs_config* cfg);
  * Positions before the start of a block count as zero; the tap softmax is
  * not renormalised there.
  */
-int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm,
+DFS_API int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm,
              void* y, float* y_f32, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -132,15 +146,20 @@ int dfs_conv(const dfs_config* cfg, const void* h, const void* wg_cm,
  *                256-B aligned
  * Layer results equal dfs_conv on each layer alone.
  */
-int dfs_conv_layers(const dfs_config* cfg, int32_t layers, const void* h,
+DFS_API int dfs_conv_layers(const dfs_config* cfg, int32_t layers, const void* h,
                     const void* wg_cm, void* y, void* ws, size_t ws_bytes,
                     void* stream);
 
 /* Workspace bytes dfs_conv_layers needs (0 if cfg or layers is invalid). */
-size_t dfs_conv_layers_workspace_size(const dfs_config* cfg, int32_t layers);
+DFS_API size_t dfs_conv_layers_workspace_size(const dfs_config* cfg, int32_t layers);
 
 /*
- * Steps 2-3: vocabulary head, log-softmax and per-slot top-K for every row.
+ * Steps 2-3: vocabulary head, log-softmax and per-slot top-K for every row
+ * (vLLM release-note article on DFlash2, section "two additions": the
+ * selector works on the K tokens the target head scores highest at each
+ * slot, in place of a per-slot argmax; its cost section sizes this stage:
+ * hidden 5120, vocabulary 248 320, K 16, the vocabulary top-k done by a
+ * dedicated kernel).
  *
  *   logit[row, v] = sum_c y[row, c] * W[v, c]           (fp32 accumulation)
  *   lse[row]      = log sum_v exp(logit[row, v])
@@ -163,16 +182,18 @@ size_t dfs_conv_layers_workspace_size(const dfs_config* cfg, int32_t layers);
  * K (K <= 16) or ranks every slice of the logits (K > 16).  Both modes give
  * the same bits.
  */
-int dfs_head_topk(const dfs_config* cfg, const void* y, const void* W,
+DFS_API int dfs_head_topk(const dfs_config* cfg, const void* y, const void* W,
                   int32_t* cand_ids, float* cand_logp, float* lse,
                   float* logits_f32, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Step 3 alone, on caller-supplied fp32 logits [rows, V] (any finite values
- * or -inf; a row of all -inf yields lse = -inf and NaN scores).  Same outputs
- * and ordering as dfs_head_topk.  cfg->dtype is ignored.
+ * or -inf; a row of all -inf yields lse = -inf and NaN scores): the per-slot
+ * vocabulary top-k and log-softmax of the release-note article's cost
+ * section, which times that top-k as a kernel of its own on given logits.
+ * Same outputs and ordering as dfs_head_topk.  cfg->dtype is ignored.
  */
-int dfs_topk_logits(const dfs_config* cfg, const float* logits,
+DFS_API int dfs_topk_logits(const dfs_config* cfg, const float* logits,
                     int32_t* cand_ids, float* cand_logp, float* lse,
                     void* ws, size_t ws_bytes, void* stream);
 
@@ -240,17 +261,21 @@ typedef struct {
  * outside [0, V) gets path = -1 in every slot, path_idx = -1 and
  * path_score = NaN; the other blocks are unaffected.
  */
-int dfs_select(const dfs_config* cfg, const dfs_select_opts* opts,
+DFS_API int dfs_select(const dfs_config* cfg, const dfs_select_opts* opts,
                const int32_t* anchor, const int32_t* cand_ids, const float* cand_logp,
                const void* P, const void* Q, int32_t* path, float* path_score,
                int32_t* path_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The whole block: dfs_conv -> dfs_head_topk -> dfs_select on one stream.
+ * The whole block: dfs_conv -> dfs_head_topk -> dfs_select on one stream
+ * (release-note article, section "two additions": the hidden states of one
+ * block and the verified anchor in, one proposed path out; Inco AI post,
+ * section "lightweight path selector": scoring is parallel over all slots,
+ * and the walk is the only sequential part).
  * cand_ids / cand_logp are optional outputs (NULL: kept in the workspace).
  * Arguments as above.
  */
-int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts,
+DFS_API int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts,
                     const void* h, const int32_t* anchor,
                     const void* wg_cm, const void* W, const void* P, const void* Q,
                     int32_t* path, float* path_score, int32_t* cand_ids,

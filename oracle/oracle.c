@@ -128,8 +128,9 @@ int orc_conv(const orc_shape* s, const void* h, const void* wg,
 }
 
 /* ---- steps 5-6: log-softmax and top-K ------------------------------------- */
-/* The selector keeps the target head's top-K per slot (release-note article,
- * "two additions"); its node score is the candidate's log-probability.
+/* The selector works on the K highest-ranked tokens of the target head at
+ * each slot (release-note article, "two additions"); its node score is the
+ * candidate's log-probability.
  * Order: larger logit first, equal logits by smaller vocabulary id. */
 static int better(const double* L, int a, int b)
 {
@@ -169,8 +170,9 @@ int orc_topk(int nr, int V, int K, const double* logits,
 
 /* ---- step 4: vocabulary head --------------------------------------------- */
 /* Logits of every row of the block against the shared target head
- * (release-note article: "the target head's top-K"; RTX 4090 report: the
- * drafter shares embedding and lm_head with the target). */
+ * (release-note article, "two additions": the candidates come from the
+ * target's head; RTX 4090 report: the drafter shares embedding and lm_head
+ * with the target). */
 int orc_head(const orc_shape* s, const void* y, const void* W, int r0, int nr,
              double* logits, double* lse, int32_t* ids, double* logp)
 {
@@ -240,8 +242,9 @@ int orc_transitions(const orc_shape* s, int32_t anchor, const int32_t* ids,
 }
 
 /* ---- step 8: best path from the anchor (max-sum Viterbi) ------------------ */
-/* Release-note article: walk the best path from the verified anchor over the
- * per-slot candidates.  Path score = sum over draft slots of the node score
+/* Release-note article, "two additions": the selector picks the
+ * highest-scoring path through the per-slot candidates, starting at the
+ * accepted anchor.  Path score = sum over draft slots of the node score
  * plus the transition score from the previous slot's choice (the anchor for
  * slot 1).  Ties: the lowest predecessor index, and the lowest final index. */
 int orc_viterbi(int B, int K, const double* logp, const double* T,

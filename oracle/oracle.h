@@ -10,10 +10,12 @@
  *
  * Sources (web pages, cited by title and section):
  *  - vLLM release-note article on DFlash2 (page 1), section "two additions":
- *    a grouped dynamic depthwise convolution inside each block lets a draft
- *    position see the earlier positions without another backbone pass; the
- *    candidate selector keeps the target head's top-K per slot, scores
- *    adjacent transitions and walks the best path from the verified anchor.
+ *    each block gets a grouped, dynamically generated depthwise convolution
+ *    through which a draft position sees the earlier positions of its block
+ *    without running the backbone again; the candidate selector replaces the
+ *    per-slot argmax: it retains the target head's K best tokens at every
+ *    slot, scores transitions between neighbouring slots, and walks the
+ *    best-scoring path onward from the anchor that verification accepted.
  *  - Inco AI post "DFlash 2: keep the draft parallel" (page 4), section
  *    "lightweight path selector": the score of candidate b after a is
  *    S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)> with 256-wide per-token

@@ -32,6 +32,9 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert n in exported, n
         assert hasattr(dfs.lib(), n)
+    # and nothing else: the library's internal functions stay hidden
+    every_text_symbol = set(re.findall(r"\bT (\S+)$", out, re.M))
+    assert every_text_symbol == set(names), sorted(every_text_symbol - set(names))[:5]
 
 
 def test_status_strings():
