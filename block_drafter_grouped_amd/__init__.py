@@ -11,12 +11,14 @@ from .dflash2 import (  # noqa: F401
     Config,
     DFSError,
     STATUS,
+    STATIC_WORKSPACE_BYTES,
     SelectOpts,
     WALKS,
     conv,
     conv_layers,
     conv_layers_workspace_size,
     draft_block,
+    draft_block_static,
     head_topk,
     lib,
     select,

@@ -28,7 +28,9 @@ STATUS = {
 
 EXPORTS = ("dfs_workspace_size", "dfs_status_string", "dfs_validate_config", "dfs_conv",
            "dfs_conv_layers", "dfs_conv_layers_workspace_size",
-           "dfs_head_topk", "dfs_topk_logits", "dfs_select", "dfs_draft_block")
+           "dfs_head_topk", "dfs_topk_logits", "dfs_select", "dfs_draft_block", "dfs_draft_block_static")
+
+STATIC_WORKSPACE_BYTES = 64 << 20  # DFS_STATIC_WORKSPACE_BYTES
 
 
 class Config(C.Structure):
@@ -95,6 +97,7 @@ def _load():
     lib_.dfs_topk_logits.argtypes = [cfg, P, P, P, P, P, S, P]
     lib_.dfs_select.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, S, P]
     lib_.dfs_draft_block.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib_.dfs_draft_block_static.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, P, P]
     for n in EXPORTS[2:]:
         getattr(lib_, n).restype = I
     return lib_
@@ -185,3 +188,13 @@ def draft_block(cfg, h, anchor, wg_cm, W, P, Q, path, path_score, ws, cand_ids=N
                                 _ptr(wg_cm), _ptr(W), _ptr(P), _ptr(Q), _ptr(path), _ptr(path_score),
                                 _ptr(cand_ids), _ptr(cand_logp), _ptr(ws), _nbytes(ws), _stream(stream)),
            "dfs_draft_block")
+
+
+def draft_block_static(cfg, h, anchor, wg_cm, W, P, Q, path, path_score, cand_ids=None, cand_logp=None,
+                       stream=None, gate=None, walk="viterbi", temperature=1.0, uniforms=None):
+    """dfs_draft_block_static: draft_block() on the library's static
+    per-device workspace (no workspace argument, nothing allocated)."""
+    _check(_lib.dfs_draft_block_static(C.byref(cfg), _opts(gate, walk, temperature, uniforms), _ptr(h),
+                                       _ptr(anchor), _ptr(wg_cm), _ptr(W), _ptr(P), _ptr(Q), _ptr(path),
+                                       _ptr(path_score), _ptr(cand_ids), _ptr(cand_logp), _stream(stream)),
+           "dfs_draft_block_static")

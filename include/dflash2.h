@@ -44,7 +44,8 @@
  *  - Ownership: the caller owns every buffer, including the workspace
  *    (>= dfs_workspace_size(cfg) bytes; contents undefined between calls;
  *    one call at a time per workspace).  The library keeps no state besides
- *    the kernels' LDS attributes (set once per process).
+ *    the kernels' LDS attributes (set once per process) and, for
+ *    dfs_draft_block_static only, its static per-device workspace.
  *  - Errors: the return value is a dfs_status.  All argument checks happen on
  *    the host BEFORE any HIP call, so a rejected call touches no device
  *    state.  DFS_ERR_HIP reports a failed kernel launch; faults inside a
@@ -280,6 +281,33 @@ DFS_API int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts,
                     const void* wg_cm, const void* W, const void* P, const void* Q,
                     int32_t* path, float* path_score, int32_t* cand_ids,
                     float* cand_logp, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Allocation-free variant of dfs_draft_block, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, checks, kernels and
+ * results as dfs_draft_block, but no workspace argument: the workspace is a
+ * static device buffer of the library, DFS_STATIC_WORKSPACE_BYTES per GPU,
+ * held from the library's load until the process ends.  The call allocates
+ * and frees nothing.
+ *  - Configurations with dfs_workspace_size(cfg) > DFS_STATIC_WORKSPACE_BYTES
+ *    are rejected with DFS_ERR_WORKSPACE, before any HIP call (every
+ *    configuration up to 8 rows with K <= 16 fits, at any vocabulary and
+ *    hidden size; larger ones when their written logits fit).
+ *  - The buffer of the CURRENT device is used; `stream` must belong to it.
+ *    The first call on a device resolves that buffer's address (a HIP symbol
+ *    query, no allocation); make it outside stream capture.
+ *  - Every call on one GPU shares that GPU's buffer, which keeps what the
+ *    last call left there (no part of it has to start at zero).  Calls that
+ *    overlap on one GPU (two streams, or two threads) race on it: serialise
+ *    them.
+ */
+#define DFS_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+DFS_API int dfs_draft_block_static(const dfs_config* cfg, const dfs_select_opts* opts,
+                                   const void* h, const int32_t* anchor,
+                                   const void* wg_cm, const void* W, const void* P,
+                                   const void* Q, int32_t* path, float* path_score,
+                                   int32_t* cand_ids, float* cand_logp, void* stream);
 
 #ifdef __cplusplus
 }

@@ -237,3 +237,24 @@ def test_binding_raises_typed_error():
     with pytest.raises(dfs.DFSError) as e:
         dfs.conv(c, A, A, A, None, stream=0)
     assert e.value.status == SHAPE and "DFS_ERR_SHAPE" in str(e.value)
+
+
+def test_static_entry_point_host_checks():
+    """dfs_draft_block_static: the same host checks as dfs_draft_block, and a
+    configuration whose workspace exceeds the static buffer is refused with
+    DFS_ERR_WORKSPACE before any HIP call (fake pointers: nothing launches)."""
+    import re as _re
+    m = _re.search(r"#define DFS_STATIC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == dfs.STATIC_WORKSPACE_BYTES
+    f = dfs.lib().dfs_draft_block_static
+    big = cfg_of(3)  # batch 32 at the page vocabulary: written logits of 254 MB
+    assert dfs.workspace_size(big) > dfs.STATIC_WORKSPACE_BYTES
+    args = [A] * 10 + [None, None, None]  # h, anchor, wg, W, P, Q, path, score; cand buffers; stream
+    assert f(C.byref(big), None, *args[:8], None, None, None) == WS
+    small = cfg_of(2)
+    assert dfs.workspace_size(small) <= dfs.STATIC_WORKSPACE_BYTES
+    assert f(C.byref(small), None, None, *args[1:8], None, None, None) == NULL
+    assert f(C.byref(small), None, A + 8, *args[1:8], None, None, None) == MISAL
+    assert f(C.byref(cfg_of(2, top_k=0)), None, *args[:8], None, None, None) == SHAPE
+    bad_walk = dfs.SelectOpts(None, 7, 1.0, None)
+    assert f(C.byref(small), C.byref(bad_walk), *args[:8], None, None, None) == UNSUP
