@@ -21,7 +21,8 @@ import workloads as wl  # noqa: E402
 from plant import apply_plant, plant_pairs  # noqa: E402
 
 
-def main():
+def compute():
+    """The fixture's content, from the seeded generators and the oracle."""
     s = wl.shape_of(4)
     t0 = time.time()
     inp = wl.make_inputs(4)
@@ -55,6 +56,12 @@ def main():
         "n_sites_deviating": len(deviating),
         "n_blocks_off_argmax": int(sum(res["path"][b].tolist() != argmax_paths[b] for b in range(s.batch))),
     }
+    return out
+
+
+def main():
+    out = compute()
+    s = wl.shape_of(4)
     path = os.path.join(ROOT, "tests", "golden", "plant_w4.json")
     json.dump(out, open(path, "w"))
     print(f"{out['n_sites']} sites, {out['n_sites_deviating']} deviate from the argmax; "

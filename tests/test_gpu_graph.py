@@ -1,5 +1,6 @@
 """A whole draft block captured in a HIP graph (through torch.cuda.graph) and
-replayed: every replay must reproduce the eager result bit for bit.  The
+replayed: every replay is compared with the oracle on the same seeded
+inputs, and must reproduce the eager result bit for bit.  The
 library allocates, frees and synchronises nothing and takes the caller's
 stream, so a caller can capture a step to cut launch overhead on
 launch-bound shapes.  Between replays the test runs its own eager work
@@ -15,6 +16,8 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 import block_drafter_grouped_amd as dfs  # noqa: E402
+import e2e_check as e2e  # noqa: E402
+import oracle as orc  # noqa: E402
 
 
 def S(**kw):
@@ -67,5 +70,6 @@ def test_draft_block_graph_replay(s):
         g.replay()
         torch.cuda.synchronize()
         got = [from_dev(t) for t in (path, score, ids, lp)]
+        e2e.check_block_e2e(orc, s, inp, got)
         for a, b in zip(got, want):
             assert np.array_equal(a, b, equal_nan=True), f"replay {rep}"

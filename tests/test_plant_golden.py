@@ -2,6 +2,8 @@
 import json
 import os
 
+import pytest
+
 import workloads as wl
 
 G = os.path.join(os.path.dirname(__file__), "golden", "plant_w4.json")
@@ -28,3 +30,21 @@ def test_plants_move_the_oracle_walk():
     assert g["n_blocks_off_argmax"] >= 1
     for b, path in enumerate(g["path"]):
         assert path[0] == g["argmax_path"][b][0]
+
+
+@pytest.mark.slow
+def test_fixture_recomputes_from_the_oracle():
+    """The stored fixture equals what the oracle computes now from the seeded
+    inputs (candidates, lse, paths, indices, scores, margins and counts), so
+    a change to the oracle or the generators cannot leave it stale.  About a
+    minute on 8 cores."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "make_plant_w4", os.path.join(os.path.dirname(__file__), "golden", "make_plant_w4.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    fresh = json.loads(json.dumps(mod.compute()))
+    stored = json.load(open(G))
+    assert fresh.keys() == stored.keys()
+    for k in stored:
+        assert fresh[k] == stored[k], k
