@@ -108,9 +108,12 @@ def cpu_baseline(s, inp, budget_s: float) -> dict:
             "sample": f"{n} full call(s) of the same workload ({blocks} blocks) in {el:.1f} s; CPU: {cpu_model()}"}
 
 
-def graph_replay_ms(step, stream, steps: int) -> float:
-    """Milliseconds per step when the step is captured once in a HIP graph and
-    replayed ``steps`` times, timed on ``stream``."""
+def graph_replay_ms(step, stream, steps: int, per_graph: int = 20) -> float:
+    """Milliseconds per step when ``per_graph`` steps are captured back to
+    back in one HIP graph and the graph is replayed until at least ``steps``
+    steps ran, timed on ``stream``.  With several steps per replay the
+    host's cost of issuing a replay is spread over them, so for shapes whose
+    GPU work is shorter than a host call this measures the GPU."""
     import torch
 
     gstream = torch.cuda.Stream()
@@ -121,47 +124,87 @@ def graph_replay_ms(step, stream, steps: int) -> float:
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=gstream):
-        step(gstream)
+        for _ in range(per_graph):
+            step(gstream)
     torch.cuda.synchronize()
-    for _ in range(3):
+    for _ in range(2):
         graph.replay()
     torch.cuda.synchronize()
+    reps = max(1, (steps + per_graph - 1) // per_graph)
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     g0.record(stream)
-    for _ in range(steps):
+    for _ in range(reps):
         graph.replay()
     g1.record(stream)
     torch.cuda.synchronize()
-    ms = g0.elapsed_time(g1) / steps
+    ms = g0.elapsed_time(g1) / (reps * per_graph)
     del graph
     return ms
 
 
-def batch32_line(s, dev, steps: int) -> dict:
-    """The page drafter shape at batch 32 (256 rows), on the weights W, P, Q
-    and the generator of the current run (same shapes and distributions as
-    the batch-32 workload's), with that workload's hidden states and
-    anchors: per-block time and the head stage against the MFMA roofline."""
+def dev_tensor(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def head_roofline(s, us_head: float) -> dict:
+    """The lm_head + top-K stage against both roofs: algorithmic bytes (the
+    weight once, y in, candidates and lse out) over 8 TB/s, and the GEMM's
+    flops over the bf16 MFMA peak."""
+    hb, fl = head_stage_bytes(s), head_flops(s)
+    gbs = hb / (us_head * 1e-6) / 1e9
+    tfl = fl / (us_head * 1e-6) / 1e12
+    return {"head_topk_us": round(us_head, 2), "head_GBps": round(gbs, 1), "head_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "head_tflops": round(tfl, 1), "head_mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+            "bound": "latency" if s.dtype != "bf16" else ("mfma" if uses_gemm_head(s) and s.rows >= 256 else "hbm")}
+
+
+def cpu_sample(s, inp, calls: int, blocks=None) -> dict:
+    """The oracle as it is on a bounded sample of a workload: the median of
+    ``calls`` whole calls on ``blocks`` of its blocks (default: all)."""
+    import oracle
+    if blocks is not None:
+        rows = np.concatenate([np.arange(b * s.block, (b + 1) * s.block) for b in blocks])
+        s2 = s.with_(batch=len(blocks))
+        h, anchor = np.ascontiguousarray(inp["h"][rows]), inp["anchor"][blocks]
+    else:
+        s2, h, anchor = s, inp["h"], inp["anchor"]
+    times = []
+    for _ in range(calls):
+        t0 = time.perf_counter()
+        oracle.draft_block(s2, h, anchor, inp["wg"], inp["W"], inp["P"], inp["Q"])
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    return {"value": round(s2.batch / med, 3), "unit": "blocks/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"median of {calls} call(s) on {s2.batch} of the {s.batch} block(s) ({med * 1e3:.1f} ms each)"}
+
+
+def workload_line(wid: int, inp: dict, steps: int, cpu_calls: int, cpu_blocks=None, graph: bool = False) -> dict:
+    """One workload timed on its own inputs (the h, anchors and weights in
+    ``inp``): µs per block and blocks/s of whole dfs_draft_block steps, the
+    head stage against its roofs, optionally the step replayed from a HIP
+    graph, and a short oracle sample."""
     import torch
 
     import block_drafter_grouped_amd as dfs
 
-    s32 = wl.shape_of(3)
-    if (s.hidden, s.vocab, s.rank, s.top_k, s.block, s.dtype) != (s32.hidden, s32.vocab, s32.rank, s32.top_k,
-                                                                     s32.block, s32.dtype):
-        return None
-    inp = wl.make_inputs_for(s32, 3, parts=("h", "anchor"))
-    h = torch.from_numpy(np.ascontiguousarray(inp["h"]).view(np.int16)).cuda()
-    anchor = torch.from_numpy(inp["anchor"]).cuda()
-    cfg = dfs.Config.of(s32)
+    s = wl.shape_of(wid)
+    d = {k: dev_tensor(inp[k]) for k in ("h", "W", "P", "Q", "anchor")}
+    wg_cm = dev_tensor(np.ascontiguousarray(inp["wg"].T))
+    cfg = dfs.Config.of(s)
     ws = torch.empty(dfs.workspace_size(cfg), dtype=torch.uint8, device="cuda")
-    path = torch.empty((s32.batch, s32.block), dtype=torch.int32, device="cuda")
-    score = torch.empty((s32.batch,), dtype=torch.float32, device="cuda")
-    ids = torch.empty((s32.rows, s32.top_k), dtype=torch.int32, device="cuda")
-    lp = torch.empty((s32.rows, s32.top_k), dtype=torch.float32, device="cuda")
-    lse = torch.empty((s32.rows,), dtype=torch.float32, device="cuda")
-    y = torch.empty((s32.rows, s32.hidden), dtype=torch.int16, device="cuda")
+    tdt = torch.int16 if s.dtype == "bf16" else torch.float32
+    path = torch.empty((s.batch, s.block), dtype=torch.int32, device="cuda")
+    score = torch.empty((s.batch,), dtype=torch.float32, device="cuda")
+    ids = torch.empty((s.rows, s.top_k), dtype=torch.int32, device="cuda")
+    lp = torch.empty((s.rows, s.top_k), dtype=torch.float32, device="cuda")
+    lse = torch.empty((s.rows,), dtype=torch.float32, device="cuda")
+    y = torch.empty((s.rows, s.hidden), dtype=tdt, device="cuda")
     stream = torch.cuda.current_stream()
+
+    def step(st=stream):
+        dfs.draft_block(cfg, d["h"], d["anchor"], wg_cm, d["W"], d["P"], d["Q"], path, score, ws, stream=st)
 
     def timed(fn, n) -> float:
         for _ in range(3):
@@ -174,16 +217,20 @@ def batch32_line(s, dev, steps: int) -> dict:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n * 1e3  # us
 
-    us_step = timed(lambda: dfs.draft_block(cfg, h, anchor, dev["wg_cm"], dev["W"], dev["P"], dev["Q"], path,
-                                            score, ws), steps)
-    dfs.conv(cfg, h, dev["wg_cm"], y, ws)
-    us_head = timed(lambda: dfs.head_topk(cfg, y, dev["W"], ids, lp, lse, ws), steps)
-    fl = head_flops(s32)
-    return {"workload": WORKLOAD_NAMES[3], "steps": steps, "us_per_block": round(us_step / s32.batch, 3),
-            "blocks_per_s": round(s32.batch / (us_step * 1e-6), 1), "head_topk_us": round(us_head, 2),
-            "head_tflops": round(fl / (us_head * 1e-6) / 1e12, 1),
-            "head_mfma_frac": round(fl / (us_head * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "note": "W, P, Q and the conv generator of this run; h and anchors of the batch-32 workload"}
+    us_step = timed(step, steps)
+    dfs.conv(cfg, d["h"], wg_cm, y, ws)
+    us_head = timed(lambda: dfs.head_topk(cfg, y, d["W"], ids, lp, lse, ws), steps)
+    out = {"workload": WORKLOAD_NAMES[wid], "steps": steps, "us_per_block": round(us_step / s.batch, 3),
+           "us_per_step": round(us_step, 2), "blocks_per_s": round(s.batch / (us_step * 1e-6), 1),
+           **head_roofline(s, us_head), "outside_head_us": round(us_step - us_head, 2)}
+    if graph:
+        ms_g = graph_replay_ms(step, stream, steps)
+        out["graph"] = {"us_per_step": round(ms_g * 1e3, 2), "blocks_per_s": round(s.batch / (ms_g * 1e-3), 1),
+                        "note": "20 steps per captured HIP graph"}
+    if cpu_calls > 0:
+        out["cpu_baseline"] = cpu_sample(s, inp, cpu_calls, cpu_blocks)
+    del d, wg_cm, ws
+    return out
 
 
 def main() -> int:
@@ -295,8 +342,21 @@ def main() -> int:
         us_shard = timed(lambda: dfs.head_topk(cfg8, y, W[:vs], ids, lp, lse, ws8, stream=stream))
         del ws8
 
-    b32 = None if args.no_extras or args.workload == 3 else batch32_line(
-        s, {"W": W, "P": P, "Q": Q, "wg_cm": wg_cm}, max(10, min(args.steps, 50)))
+    # The other workloads, each on its own seeded inputs: µs per block, the
+    # head stage against both roofs, the step replayed from a HIP graph for
+    # the launch-bound shapes, and a short oracle sample.
+    others = None
+    if not args.no_extras:
+        others = {}
+        plan = {0: (500, 5, None, True), 1: (200, 5, None, True), 3: (30, 1, [0, 1], False),
+                4: (30, 1, [0], False)}
+        for wid, (n, calls, blocks, with_graph) in plan.items():
+            if wid == args.workload:
+                continue
+            winp = wl.make_inputs(wid)
+            others[str(wid)] = workload_line(wid, winp, n, calls if args.cpu_seconds > 0 else 0, blocks,
+                                             graph=with_graph)
+            del winp
 
     hb = head_stage_bytes(s)
     traffic = recorded_traffic(args.workload)
@@ -352,8 +412,8 @@ def main() -> int:
         "wall_s_timed": round(wall, 3),
         "graph": None if ms_graph is None else
         {"ms_per_step": round(ms_graph, 5), "value": round(s.batch / (ms_graph * 1e-3), 2),
-         "note": "the same step replayed from one captured HIP graph"},
-        "batch32": b32,
+         "note": "20 steps captured back to back in one HIP graph, replayed"},
+        "workloads": others,
         "roofline": roof,
         "cpu_baseline": None,
     }

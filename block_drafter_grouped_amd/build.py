@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdflash2.so")
-SOURCES = ["conv.hip", "head.hip", "gemm_head.hip", "slice_topk.hip", "select.hip", "static_ws.hip", "api.cpp"]
+SOURCES = ["conv.hip", "head.hip", "gemm_head.hip", "slice_topk.hip", "select.hip", "block_small.hip", "static_ws.hip", "api.cpp"]
 ARCH = os.environ.get("DFS_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 ops are switched off for all device code.  Code object v5 is

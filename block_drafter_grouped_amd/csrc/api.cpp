@@ -201,8 +201,12 @@ int launch_draft_block(const dfs_config* cfg, const SelectOpts& o, const void* h
                        const void* wg_cm, const void* W, const void* P, const void* Q, int32_t* path,
                        float* path_score, int32_t* cand_ids, float* cand_logp, char* w, void* stream) {
     const Dims d = dims_of(cfg);
-    const WsLayout L = ws_layout(d);
     hipStream_t s = (hipStream_t)stream;
+    // Small, launch-bound shapes: the whole block in one launch.
+    if (use_small_block(d))
+        return hip_status(
+            launch_block_small(d, o, h, anchor, wg_cm, W, P, Q, path, path_score, cand_ids, cand_logp, s));
+    const WsLayout L = ws_layout(d);
     int st;
     // One tap: the conv is the identity, so the head reads h directly.
     const void* y = d.ks == 1 ? h : (const void*)(w + L.y);

@@ -18,12 +18,15 @@ namespace {
 // logit[v][row] = <W[v], y[row]> on v_mfma_f32_32x32x16_bf16 that writes
 // the fp32 logits (and, MS, the segment partials described below).
 //  - One persistent workgroup per CU owns a contiguous vocabulary range and
-//    walks it in tiles of 256 rows of W against every hidden row, in stages
-//    of KC channels (64 when D % 64 == 0, else 32).
-//  - Producer and consumer waves.  The NWB consumer waves split the 256
-//    vocabulary rows x 32 NWB hidden rows of a tile into blocks of NVB x
-//    (8 / NVB) accumulator tiles of 32x32 each (8 x 1 at 256 rows, 4 x 2
-//    below); they only read LDS, issue MFMAs and store logits.  Four
+//    walks it in tiles of TV = 32 TVB rows of W (256 or 512) against a pass
+//    of RP hidden rows, in stages of KC channels (64 when D % 64 == 0, else
+//    32).
+//  - Producer and consumer waves.  The NWB consumer waves split the TV
+//    vocabulary rows x RP hidden rows of a tile into blocks of NVB x
+//    (8 / NVB) accumulator tiles of 32x32 each; they only read LDS, issue
+//    MFMAs and store logits.  Every consumer holds 8 accumulator tiles, so
+//    a wider vocabulary tile serves fewer hidden rows per pass and re-reads
+//    them fewer times per weight byte.  Four
 //    producer waves move the operands by direct global->LDS loads, two for W
 //    (a ring of RW stages) and two for the hidden rows (RY stages; L2
 //    resident, so a shallower ring).  A wave's count of outstanding memory
@@ -53,7 +56,6 @@ namespace {
 // whose plain stores cost a tenth of the weight stream.  The kernel keeps
 // the stores and adds only the (max, sum of exp) of each segment, which
 // lets the merge read a few segments of the written logits per row.
-constexpr int kGemmTV = 256;
 
 template <int KC>
 __device__ __forceinline__ int gemm_swz(int row) {
@@ -140,15 +142,28 @@ __device__ __forceinline__ float sum_of_half(float x) {
     return x + swap_rows_of_half(x);
 }
 
-template <int NWB, int KC, int RW, int RY, int NVB, bool RS, bool MS>
+// Consumer layout of a configuration: NVW waves across the TV vocabulary
+// rows of a tile, NRW across the RP hidden rows of a pass.
+template <int NWB, int NVB, int TVB>
+struct GemmShape {
+    static constexpr int TV = 32 * TVB;
+    static constexpr int NRB = 8 / NVB;
+    static constexpr int NVW = TVB / NVB;
+    static constexpr int NRW = NWB / NVW;
+    static constexpr int RP = 32 * NRB * NRW;
+    static_assert(NVB * NRB == 8 && TVB % NVB == 0 && NWB % NVW == 0 && NRW >= 1, "consumer layout");
+};
+
+template <int NWB, int KC, int RW, int RY, int NVB, int TVB, bool RS, bool MS>
 __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kernel(
     const uint16_t* __restrict__ y, int rows_total, int D, const uint16_t* __restrict__ W, int V, int nch,
     float* __restrict__ logits, float2* __restrict__ cms, int nt) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int RP = 32 * NWB;
+    using G = GemmShape<NWB, NVB, TVB>;
+    constexpr int TV = G::TV, RP = G::RP;
     constexpr int UPR = KC / 8;                 // 16-B units per LDS row
     constexpr int RPI = kWave / UPR;            // rows per 1-KB load instruction
-    constexpr int WBYTES = kGemmTV * KC * 2;    // one W stage
+    constexpr int WBYTES = TV * KC * 2;         // one W stage
     constexpr int YBYTES = RP * KC * 2;         // one hidden-row stage
     constexpr int WI = WBYTES / 1024 / 2;       // load instructions per W producer per stage
     constexpr int YI = YBYTES / 1024 / 2;       // per hidden-row producer per stage
@@ -161,7 +176,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
     const int64_t T32 = ((int64_t)V + 31) / 32;
     const int b_beg = (int)(T32 * c / nch), b_end = (int)(T32 * (c + 1) / nch);
     const int v_beg = b_beg * 32, v_end = min(b_end * 32, V);
-    const int ntiles = (b_end - b_beg + 7) / 8;
+    const int ntiles = (b_end - b_beg + TVB - 1) / TVB;
     const int total = ntiles * S;
     const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
     const uint32_t ybase = smem_base + RW * WBYTES;
@@ -177,15 +192,15 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
         // covers tile rows RPI n .. RPI n + RPI - 1 and is skipped when all of
         // them lie past the range (the last tile of the range).
         auto w_count = [&](int g) {
-            const int nv = min(kGemmTV, v_end - (v_beg + (g / S) * kGemmTV));
+            const int nv = min(TV, v_end - (v_beg + (g / S) * TV));
             int cnt = 0;
 #pragma unroll
             for (int i = 0; i < WI; ++i) cnt += (RPI * (pw + 2 * i) < nv) ? 1 : 0;
             return cnt;
         };
         auto issue_w = [&](int g) {
-            const int k0 = (g % S) * KC, v0 = v_beg + (g / S) * kGemmTV;
-            const int nv = min(kGemmTV, v_end - v0);
+            const int k0 = (g % S) * KC, v0 = v_beg + (g / S) * TV;
+            const int nv = min(TV, v_end - v0);
             const uint32_t base = smem_base + (uint32_t)((g % RW) * WBYTES);
 #pragma unroll
             for (int i = 0; i < WI; ++i) {
@@ -236,12 +251,11 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
     }
 
     // Consumers.  Wave w computes NVB vocabulary blocks x NRB row blocks of
-    // 32x32 (NVB * NRB = 8): vocabulary blocks NVB * (w % (8 / NVB)) .., row
-    // blocks NRB * (w / (8 / NVB)) ..; 8 / NVB waves span the 256 vocabulary
-    // rows, and the NWB waves the 32 NWB hidden rows.  Per 16 channels a wave
-    // reads NVB + NRB operand fragments from LDS for 8 MFMAs.
-    constexpr int NRB = 8 / NVB, NVW = 8 / NVB;
-    static_assert(NVB * NRB == 8 && NWB % NVW == 0, "the consumer waves cover the 8 x NWB tiles of a stage");
+    // 32x32 (NVB * NRB = 8): vocabulary blocks NVB * (w % NVW) .., row blocks
+    // NRB * (w / NVW) ..; NVW waves span the TV vocabulary rows, NRW waves the
+    // RP hidden rows.  Per 16 channels a wave reads NVB + NRB operand
+    // fragments from LDS for 8 MFMAs.
+    constexpr int NRB = G::NRB, NVW = G::NVW;
     const int j = lane & 31, half = lane >> 5;
     const int vw = wave % NVW, rw = wave / NVW;
     // row blocks of this wave that hold rows (RS: the last row pass is
@@ -271,7 +285,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
     for (int g = 0; g < total; ++g) {
         // vocabulary blocks of this wave that hold rows of the range (the
         // last tile of the range is partial); the others are skipped
-        const int nvb = min(NVB, max(0, (v_end - (v_beg + tile * kGemmTV) - 32 * vw * NVB + 31) / 32));
+        const int nvb = min(NVB, max(0, (v_end - (v_beg + tile * TV) - 32 * vw * NVB + 31) / 32));
         __syncthreads();  // stage g published
         const uint4* sw = (const uint4*)(smem + (size_t)(g % RW) * WBYTES);
         const uint4* sy = (const uint4*)(smem + (size_t)RW * WBYTES + (size_t)(g % RY) * YBYTES);
@@ -303,7 +317,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
                 // 8 (r / 4) + 4 half + r % 4 of the block.  Entries past the
                 // range (the last tile of a list) read as -inf here; they are
                 // not stored either.
-                const int vt = v_beg + tile * kGemmTV;
+                const int vt = v_beg + tile * TV;
                 const int seg = list * nt + tile;
                 if (nvb < NVB || vt + 32 * (vw * NVB + nvb) > v_end) {
 #pragma unroll
@@ -350,7 +364,7 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
             // held one row, and a 16-B store touched 32 lines, 32 B of each.)
             // Addresses: a wave-uniform base per (row block, vocabulary block,
             // register) and one lane offset (half-wave row, entry j) for all.
-            const int vt = v_beg + tile * kGemmTV;
+            const int vt = v_beg + tile * TV;
             const uint32_t lane_off = (uint32_t)(4 * half * V + j);
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
@@ -437,14 +451,14 @@ constexpr int kSegUnroll = 16;  // logit loads in flight per thread
 constexpr int kSegRefine = 512; // at most this many live segments: tighter theta
 
 struct SegGeom {
-    int nch, nvw, nvb, nt, t32, V, span_log2;  // span: 32 nvb logits
+    int nch, nvw, nvb, nt, t32, V, span_log2, tv;  // span: 32 nvb logits; tv: tile width
     // vocabulary run [beg, end) of segment sg (list sg / nt, tile sg % nt)
     __device__ __forceinline__ void range(int sg, int& beg, int& end) const {
         const int list = sg / nt, tile = sg - list * nt;
         const int c = list / nvw, vw = list - c * nvw;
         const int vb = (int)((int64_t)t32 * c / nch) * 32;
         const int ve = min((int)((int64_t)t32 * (c + 1) / nch) * 32, V);
-        beg = vb + tile * kGemmTV + 32 * vw * nvb;
+        beg = vb + tile * tv + 32 * vw * nvb;
         end = min(beg + 32 * nvb, ve);
     }
 };
@@ -689,56 +703,80 @@ __global__ __launch_bounds__(1024) void merge_seg_kernel(const float* __restrict
 
 }  // namespace
 
-template <int NWB, int KC, int RW, int RY, int NVB, bool RS, bool MS>
+template <int NWB, int KC, int RW, int RY, int NVB, int TVB, bool RS, bool MS>
 hipError_t launch_head_gemm_t(const Dims& d, const void* y, const void* W, int nch, float* logits, float2* ms,
                               int nt, hipStream_t s) {
-    constexpr int RP = 32 * NWB;
-    constexpr size_t lds = ((size_t)RW * kGemmTV + (size_t)RY * RP) * KC * 2;
+    using G = GemmShape<NWB, NVB, TVB>;
+    constexpr size_t lds = ((size_t)RW * G::TV + (size_t)RY * G::RP) * KC * 2;
     static_assert(lds <= 160 * 1024, "the stage rings must fit in LDS");
-    auto fn = head_gemm_kernel<NWB, KC, RW, RY, NVB, RS, MS>;
+    auto fn = head_gemm_kernel<NWB, KC, RW, RY, NVB, TVB, RS, MS>;
     static LdsAttr attr;
     hipError_t e = ensure_lds(attr, (const void*)fn, (int)lds);
     if (e != hipSuccess) return e;
-    dim3 grid(nch, (d.rows() + RP - 1) / RP);
+    dim3 grid(nch, (d.rows() + G::RP - 1) / G::RP);
     fn<<<grid, (NWB + kGemmProducers) * kWave, lds, s>>>((const uint16_t*)y, d.rows(), d.D, (const uint16_t*)W, d.V,
                                                          nch, logits, ms, nt);
     return hipGetLastError();
 }
 
-constexpr int kGemmSmallRows = 64;  // at most this many rows: 64-row passes (2 consumer waves)
-
-// More than 8 rows: one pass of the GEMM head per 256 rows instead of one
+// More than 8 rows: one pass of the GEMM head per RP rows instead of one
 // weight stream per 8 rows.
 bool use_gemm_head(const Dims& d) { return d.bf16 && d.rows() > kRowsPass; }
 
-// NVB: vocabulary blocks per consumer wave.  8 x 1 blocks measured 5-7 %
-// faster than 4 x 2 with 8 consumer waves (256-row passes), and slower with
-// 2 or 4.
-template <int NWB, int KC, int RW, int RY, int NVB>
+template <int NWB, int KC, int RW, int RY, int NVB, int TVB>
 hipError_t launch_head_gemm_rs(const Dims& d, const void* y, const void* W, int nch, float* logits, float2* ms,
                                int nt, hipStream_t s) {
     // row skipping only where the last row pass is partial
-    const bool rs = d.rows() % (32 * NWB) != 0;
+    const bool rs = d.rows() % GemmShape<NWB, NVB, TVB>::RP != 0;
     if (ms) {
-        return rs ? launch_head_gemm_t<NWB, KC, RW, RY, NVB, true, true>(d, y, W, nch, logits, ms, nt, s)
-                  : launch_head_gemm_t<NWB, KC, RW, RY, NVB, false, true>(d, y, W, nch, logits, ms, nt, s);
+        return rs ? launch_head_gemm_t<NWB, KC, RW, RY, NVB, TVB, true, true>(d, y, W, nch, logits, ms, nt, s)
+                  : launch_head_gemm_t<NWB, KC, RW, RY, NVB, TVB, false, true>(d, y, W, nch, logits, ms, nt, s);
     }
-    return rs ? launch_head_gemm_t<NWB, KC, RW, RY, NVB, true, false>(d, y, W, nch, logits, nullptr, 0, s)
-              : launch_head_gemm_t<NWB, KC, RW, RY, NVB, false, false>(d, y, W, nch, logits, nullptr, 0, s);
+    return rs ? launch_head_gemm_t<NWB, KC, RW, RY, NVB, TVB, true, false>(d, y, W, nch, logits, nullptr, 0, s)
+              : launch_head_gemm_t<NWB, KC, RW, RY, NVB, TVB, false, false>(d, y, W, nch, logits, nullptr, 0, s);
 }
 
-// Vocabulary blocks per consumer wave of the configuration launch_head_gemm
-// picks (8: one wave spans the 256 tile rows; 4: two waves share them).
-static int gemm_nvb(const Dims& d) { return (d.D % 64 == 0 && d.rows() <= 128) ? 4 : 8; }
+// The configurations of the GEMM head, by hidden size and row count.  All
+// use 8 x 1 blocks per consumer wave (fewer scalar registers than 4 x 2,
+// and faster at every row count measured).
+//  - 64-channel stages (D % 64 == 0):
+//    * up to 128 rows: 512 x RP tiles (RP = 64 with 4 consumer waves, 128
+//      with 8) and a 2-deep weight ring of 64 KB stages.  Against 256 x RP
+//      tiles they read the hidden rows half as often per weight byte: at the
+//      page D and V the head + top-K stage took 452 us at 64 rows (492 with
+//      256 x 64 tiles) and 514 us at 128 rows (548 with 256 x 128 tiles, 576
+//      with those and a 4-deep ring);
+//    * more rows: 256 x 256 tiles and a 3-deep weight ring.
+//  - 32-channel stages: 256 x 128 or 256 x 256 tiles, 6-deep weight rings.
+enum GemmCfg { kG64x512x64, kG64x512x128, kG64x256x256, kG32x256x128, kG32x256x256 };
+
+static GemmCfg gemm_cfg(const Dims& d) {
+    if (d.D % 64 == 0) {
+        if (d.rows() <= 64) return kG64x512x64;
+        return d.rows() <= 128 ? kG64x512x128 : kG64x256x256;
+    }
+    return d.rows() <= 128 ? kG32x256x128 : kG32x256x256;
+}
+
+// (vocabulary blocks per wave, vocabulary blocks per tile) of a configuration
+static void gemm_blocks(GemmCfg c, int* nvb, int* tvb) {
+    switch (c) {
+        case kG64x512x64:
+        case kG64x512x128: *nvb = 8; *tvb = 16; return;
+        default: *nvb = 8; *tvb = 8; return;
+    }
+}
 
 GemmSegGeom gemm_seg_geom(const Dims& d) {
     GemmSegGeom g{};
+    int tvb = 8;
+    gemm_blocks(gemm_cfg(d), &g.nvb, &tvb);
     const int nch = head_chunks(d);
     const int64_t t32 = ((int64_t)d.V + 31) / 32;
     const int64_t per = (t32 + nch - 1) / nch;  // most 32-row blocks of one chunk
-    g.nt = (int)((per + 7) / 8);
-    g.nvb = gemm_nvb(d);
-    g.nseg = nch * (8 / g.nvb) * g.nt;
+    g.nt = (int)((per + tvb - 1) / tvb);
+    g.tv = 32 * tvb;
+    g.nseg = nch * (tvb / g.nvb) * g.nt;
     return g;
 }
 
@@ -746,14 +784,13 @@ static hipError_t head_gemm_dispatch(const Dims& d, const void* y, const void* W
                                      hipStream_t s) {
     const int nch = head_chunks(d);
     const int nt = ms ? gemm_seg_geom(d).nt : 0;
-    if (d.D % 64 == 0) {
-        if (d.rows() <= kGemmSmallRows)
-            return launch_head_gemm_rs<2, 64, 3, 2, 4>(d, y, W, nch, logits, ms, nt, s);
-        return d.rows() <= 128 ? launch_head_gemm_rs<4, 64, 3, 2, 4>(d, y, W, nch, logits, ms, nt, s)
-                               : launch_head_gemm_rs<8, 64, 3, 2, 8>(d, y, W, nch, logits, ms, nt, s);
+    switch (gemm_cfg(d)) {
+        case kG64x512x64: return launch_head_gemm_rs<4, 64, 2, 2, 8, 16>(d, y, W, nch, logits, ms, nt, s);
+        case kG64x512x128: return launch_head_gemm_rs<8, 64, 2, 2, 8, 16>(d, y, W, nch, logits, ms, nt, s);
+        case kG64x256x256: return launch_head_gemm_rs<8, 64, 3, 2, 8, 8>(d, y, W, nch, logits, ms, nt, s);
+        case kG32x256x128: return launch_head_gemm_rs<4, 32, 6, 4, 8, 8>(d, y, W, nch, logits, ms, nt, s);
+        default: return launch_head_gemm_rs<8, 32, 6, 4, 8, 8>(d, y, W, nch, logits, ms, nt, s);
     }
-    return d.rows() <= 128 ? launch_head_gemm_rs<4, 32, 6, 4, 8>(d, y, W, nch, logits, ms, nt, s)
-                           : launch_head_gemm_rs<8, 32, 6, 4, 8>(d, y, W, nch, logits, ms, nt, s);
 }
 
 hipError_t launch_head_gemm(const Dims& d, const void* y, const void* W, float* logits, float2* seg_ms,
@@ -765,7 +802,8 @@ hipError_t launch_merge_segs(const Dims& d, const float* logits, const float2* s
                              float* cand_logp, float* lse, hipStream_t s) {
     const GemmSegGeom g = gemm_seg_geom(d);
     const int nch = head_chunks(d);
-    const SegGeom gm{nch, 8 / g.nvb, g.nvb, g.nt, (int)(((int64_t)d.V + 31) / 32), d.V, g.nvb == 8 ? 8 : 7};
+    const SegGeom gm{nch, g.tv / (32 * g.nvb), g.nvb, g.nt, (int)(((int64_t)d.V + 31) / 32), d.V,
+                     g.nvb == 8 ? 8 : 7, g.tv};
     merge_seg_kernel<<<d.rows(), 1024, 0, s>>>(logits, seg_ms, gm, d.K, cand_ids, cand_logp, lse);
     return hipGetLastError();
 }

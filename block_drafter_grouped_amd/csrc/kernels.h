@@ -88,7 +88,7 @@ hipError_t launch_head_f32(const Dims& d, const void* y, const void* W, float* l
 // chunk's vocabulary range).  With seg_ms non-null the GEMM also writes the
 // (max, sum of exp) of every segment, layout [row][nseg].
 struct GemmSegGeom {
-    int nt, nvb, nseg;  // tiles per list, vocabulary blocks per wave, segments per row
+    int nt, nvb, nseg, tv;  // tiles per list, vocabulary blocks per wave, segments per row, tile width
 };
 GemmSegGeom gemm_seg_geom(const Dims& d);
 // Written logits + segment partials -> sorted candidates, log-probabilities
@@ -113,6 +113,15 @@ struct SelectOpts {
     float temperature;
     const float* uniforms;
 };
+
+// The whole draft block in one launch (one workgroup per block, every step
+// in LDS) for small, launch-bound shapes: block <= 16, K <= 16, hidden <= 512,
+// vocabulary <= 1024 with vocabulary x hidden <= 2^17 and block x vocabulary
+// <= 2^14, rank <= 512.
+bool use_small_block(const Dims& d);
+hipError_t launch_block_small(const Dims& d, const SelectOpts& o, const void* h, const int32_t* anchor,
+                              const void* wg_cm, const void* W, const void* P, const void* Q, int32_t* path,
+                              float* path_score, int32_t* cand_ids, float* cand_logp, hipStream_t s);
 
 hipError_t launch_select(const Dims& d, const SelectOpts& o, const int32_t* anchor, const int32_t* cand_ids,
                          const float* cand_logp, const void* P, const void* Q, int32_t* path, float* path_score,

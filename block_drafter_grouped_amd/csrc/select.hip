@@ -7,8 +7,8 @@
 // section "two additions").  The post's context gate H(h_t) is optional: the
 // caller supplies it, or it is 1.
 //
-// Fast path (bf16 tables, K <= 16, r % 32 == 0, no gate; any walk): select_fused_kernel,
-// below.  General path:
+// Fast path (bf16 tables, K <= 16, r % 32 == 0; any walk, with or without a
+// gate): select_fused_kernel, below.  General path:
 // sel_dots: one workgroup per (draft slot, block, 16 x 16 sub-tile) computes
 // the K x K matrix
 //   T_t[j, k] = sum_i P[c_{t-1, j}, i] * H_t[i] * Q[c_{t, k}, i]
@@ -18,6 +18,7 @@
 //   sampled) from LDS, with T streamed in ahead of the walk.
 #include "common.h"
 #include "kernels.h"
+#include "walk.h"
 
 namespace dfs {
 
@@ -115,15 +116,6 @@ __global__ __launch_bounds__(256) void sel_dots_kernel(const int32_t* __restrict
     }
     const int j = j0 + jb, k = k0 + kb;
     if (j < nprev && k < K) Tout[(((size_t)b * (B - 1) + t - 1) * K + j) * K + k] = acc;
-}
-
-// A block whose anchor or candidates are invalid: path -1, score NaN.
-__device__ __forceinline__ void write_bad_block(int b, int B, int32_t* path, float* path_score, int32_t* path_idx) {
-    for (int t = threadIdx.x; t < B; t += blockDim.x) {
-        path[(size_t)b * B + t] = -1;
-        if (path_idx) path_idx[(size_t)b * B + t] = -1;
-    }
-    if (threadIdx.x == 0) path_score[b] = __int_as_float(0x7FC00000);
 }
 
 // The walk over precomputed transition scores, one workgroup per block.
@@ -316,20 +308,21 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const int32_t* __res
     if (tid == 0) path_score[b] = score_s;
 }
 
-// Transition scores and the walk of one block, from candidates already in
-// LDS: Cs[t][k] (ids) and Ls[t][k] (node scores) for t = 1..B-1, a valid
-// anchor, and a barrier between filling them and this call.  Every thread
-// of the workgroup calls it.  Wave w computes T_t for t = 1 + w, 1 + w + NWS,
-// ... as one 16x16 MFMA tile (A = P rows of the previous slot's candidates,
-// or of the anchor for t = 1; B = Q rows of this slot's candidates), with
-// every gather of a slot in flight at once; wave 0 then walks.
+// Transition tiles of one block on MFMA, from candidates already in LDS:
+// Cs[t][k] (ids) for t = 1..B-1, a valid anchor, and a barrier between
+// filling them and this call.  Every thread of the workgroup calls it.  Wave
+// w computes T_t for t = 1 + w, 1 + w + NWS, ... as one 16x16 MFMA tile
+// (A = P rows of the previous slot's candidates, or of the anchor for t = 1;
+// B = Q rows of this slot's candidates), with every gather of a slot in
+// flight at once.  With a context gate (row gate_rows + t * r of slot t) the
+// A operand is P (*) H, formed in fp32 and split into bf16 hi + lo parts that
+// take one MFMA each, so the product keeps about 16 significant bits beyond
+// bf16 (the rounding of the split is 2^-17 relative).
 template <int NWS>
-__device__ __forceinline__ void select_block_lds(int b, int a, const int32_t (*Cs)[16], const float (*Ls)[16],
-                                                 float (*Ts)[16][16], uint8_t (*bp)[16], int mode, float inv_t,
-                                                 const float* Us, const uint16_t* __restrict__ P,
-                                                 const uint16_t* __restrict__ Q, int32_t* __restrict__ path,
-                                                 float* __restrict__ path_score, int32_t* __restrict__ path_idx,
-                                                 int B, int K, int r) {
+__device__ __forceinline__ void transition_tiles_mfma(int a, const int32_t (*Cs)[16], float (*Ts)[16][16],
+                                                      const uint16_t* __restrict__ P,
+                                                      const uint16_t* __restrict__ Q,
+                                                      const float* __restrict__ gate_rows, int B, int K, int r) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int i16 = lane & 15, q = lane >> 4, kk = min(i16, K - 1);
     const int nks = r / 32;
@@ -339,118 +332,70 @@ __device__ __forceinline__ void select_block_lds(int b, int a, const int32_t (*C
         const uint16_t* pr = P + (size_t)pa * r + 8 * q;
         const uint16_t* qr = Q + (size_t)qb * r + 8 * q;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < nks; s0 += 8) {
-            bf16x8 av[8], bv[8];
+        if (!gate_rows) {
+            for (int s0 = 0; s0 < nks; s0 += 8) {
+                bf16x8 av[8], bv[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int s = min(s0 + u, nks - 1);
-                av[u] = *(const bf16x8*)(pr + 32 * s);
-                bv[u] = *(const bf16x8*)(qr + 32 * s);
+                for (int u = 0; u < 8; ++u) {
+                    const int s = min(s0 + u, nks - 1);
+                    av[u] = *(const bf16x8*)(pr + 32 * s);
+                    bv[u] = *(const bf16x8*)(qr + 32 * s);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
             }
+        } else {
+            const float* gr = gate_rows + (size_t)t * r + 8 * q;
+            for (int s0 = 0; s0 < nks; s0 += 4) {
+                uint4 pv[4];
+                bf16x8 bv[4];
+                f32x4 g0[4], g1[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (s0 + u < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
+                for (int u = 0; u < 4; ++u) {
+                    const int s = min(s0 + u, nks - 1);
+                    pv[u] = *(const uint4*)(pr + 32 * s);
+                    bv[u] = *(const bf16x8*)(qr + 32 * s);
+                    g0[u] = *(const f32x4*)(gr + 32 * s);
+                    g1[u] = *(const f32x4*)(gr + 32 * s + 4);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (s0 + u >= nks) continue;
+                    const uint32_t w4[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+                    uint16_t hi[8], lo[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t bits = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
+                        const float x = __uint_as_float(bits) * (e < 4 ? g0[u][e] : g1[u][e - 4]);
+                        hi[e] = f32_to_bf16(x);
+                        lo[e] = f32_to_bf16(x - bf16_to_f32(hi[e]));
+                    }
+                    bf16x8 ah, al;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        ah[e] = __builtin_bit_cast(__bf16, hi[e]);
+                        al[e] = __builtin_bit_cast(__bf16, lo[e]);
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv[u], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv[u], acc, 0, 0, 0);
+                }
+            }
         }
         // lane holds T_t[4q + rr][i16]
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) Ts[t - 1][4 * q + rr][i16] = acc[rr];
     }
-    __syncthreads();
-    if (wave != 0) return;
-
-    if (mode != 0) {
-        // Greedy / sampled walk (modes 1, 2), with the rules and arithmetic
-        // of walk_kernel, on the tiles in LDS: lane k = candidate k.
-        const bool on = lane < K;
-        const int k = lane & 15;
-        int prev = 0;
-        float total = 0.f;
-        for (int t = 1; t < B; ++t) {
-            const float sk = on ? Ls[t][k] + Ts[t - 1][prev][k] : -INFINITY;
-            const float m = wave_max_f32(sk);
-            int pick;
-            if (mode == 1) {
-                pick = __ffsll((unsigned long long)__ballot(on && sk == m)) - 1;
-            } else {
-                float e = on ? __expf((sk - m) * inv_t) : 0.f;
-                for (int o = 1; o < kWave; o <<= 1) {  // inclusive prefix sum in lane order
-                    const float v = __shfl_up(e, o, kWave);
-                    if (lane >= o) e += v;
-                }
-                const float tot = readlane_f32(e, K - 1);
-                const float target = Us[t] * tot;
-                const uint64_t over = __ballot(on && e > target);
-                pick = over ? __ffsll((unsigned long long)over) - 1 : K - 1;
-            }
-            total += readlane_f32(sk, pick);
-            prev = pick;
-            if (lane == 0) {
-                path[(size_t)b * B + t] = Cs[t][pick];
-                if (path_idx) path_idx[(size_t)b * B + t] = pick;
-            }
-        }
-        if (lane == 0) {
-            path[(size_t)b * B] = a;
-            if (path_idx) path_idx[(size_t)b * B] = -1;
-            path_score[b] = total;
-        }
-        return;
-    }
-
-    // Lane 16 g + k: candidate k, predecessors j = 4g .. 4g + 3.  Each lane
-    // scans its four j (the first, then a strict comparison), then two
-    // butterfly steps combine the groups, the lower j winning ties: the
-    // lowest j with the largest score, as a left-to-right scan finds it.
-    // delta[k] ends up in all four lanes of k; lane j (group 0) serves
-    // delta[j] to the next slot.
-    const int k = lane & 15, g = lane >> 4;
-    const bool on = k < K;
-    float d = on ? Ls[1][k] + Ts[0][0][k] : -INFINITY;
-    for (int t = 2; t < B; ++t) {
-        float bv = -INFINITY;
-        int bi = 4 * g;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = 4 * g + i;
-            const float dj = __shfl(d, j, kWave);
-            const float c = (j < K) ? dj + Ts[t - 1][j][k] : -INFINITY;
-            const bool gt = (i == 0) | (c > bv);
-            bv = gt ? c : bv;
-            bi = gt ? j : bi;
-        }
-#pragma unroll
-        for (int o = 16; o < kWave; o <<= 1) {
-            const float ov = __shfl_xor(bv, o, kWave);
-            const int oi = __shfl_xor(bi, o, kWave);
-            const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
-            bv = take ? ov : bv;
-            bi = take ? oi : bi;
-        }
-        d = on ? bv + Ls[t][k] : -INFINITY;
-        if (on && g == 0) bp[t][k] = (uint8_t)bi;
-    }
-    const float mx = wave_max_f32(d);
-    const uint64_t ball = __ballot(on && g == 0 && d == mx);
-    const int kb = __ffsll((unsigned long long)ball) - 1;
-    if (lane == 0) {
-        int k = kb;
-        for (int t = B - 1; t >= 1; --t) {
-            path[(size_t)b * B + t] = Cs[t][k];
-            if (path_idx) path_idx[(size_t)b * B + t] = k;
-            if (t >= 2) k = bp[t][k];
-        }
-        path[(size_t)b * B] = a;
-        if (path_idx) path_idx[(size_t)b * B] = -1;
-        path_score[b] = mx;
-    }
 }
 
-// Selector for bf16 tables with K <= 16, r % 32 == 0 and no gate, on given
-// candidates; any walk (mode 0: best path, 1: greedy, 2: sampled).
+// Selector for bf16 tables with K <= 16 and r % 32 == 0, with or without a
+// context gate, on given candidates; any walk (mode 0: best path, 1: greedy,
+// 2: sampled).
 template <int NWS>
 __global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
     const int32_t* __restrict__ anchor, const int32_t* __restrict__ cand_ids, const float* __restrict__ cand_logp,
-    const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, int mode, float temperature,
+    const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, const float* __restrict__ gate, int mode,
+    float temperature,
     const float* __restrict__ uniforms, int32_t* __restrict__ path, float* __restrict__ path_score,
     int32_t* __restrict__ path_idx, int B, int K, int r, int V) {
     extern __shared__ float Tsm[];  // [B-1][16][16]
@@ -474,8 +419,10 @@ __global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
         write_bad_block(b, B, path, path_score, path_idx);
         return;
     }
-    select_block_lds<NWS>(b, a, Cs, Ls, (float(*)[16][16])Tsm, bp, mode, 1.f / temperature, Us, P, Q, path,
-                          path_score, path_idx, B, K, r);
+    float(*Ts)[16][16] = (float(*)[16][16])Tsm;
+    transition_tiles_mfma<NWS>(a, Cs, Ts, P, Q, gate ? gate + (size_t)b * B * r : nullptr, B, K, r);
+    __syncthreads();
+    walk_block_lds(b, a, Cs, Ls, Ts, bp, mode, 1.f / temperature, Us, path, path_score, path_idx, B, K);
 }
 
 }  // namespace
@@ -486,13 +433,14 @@ hipError_t launch_select(const Dims& d, const SelectOpts& o, const int32_t* anch
     // The fused kernel gathers each wave's slots one after another: for the
     // greedy and sampled walks it is the faster path up to 16 slots, for the
     // best path at every length measured (up to 64).
-    if (!o.gate && d.bf16 && d.K <= 16 && d.r % 32 == 0 && (o.walk == 0 || d.B <= 16)) {
+    if (d.bf16 && d.K <= 16 && d.r % 32 == 0 && (o.walk == 0 || d.B <= 16)) {
         const size_t lds = (size_t)(d.B - 1) * 16 * 16 * sizeof(float);
         static LdsAttr attr;
         hipError_t e = ensure_lds(attr, (const void*)select_fused_kernel<8>, (int)lds);
         if (e != hipSuccess) return e;
         select_fused_kernel<8><<<d.batch, 8 * kWave, lds, s>>>(anchor, cand_ids, cand_logp, (const uint16_t*)P,
-                                                             (const uint16_t*)Q, o.walk, o.temperature, o.uniforms,
+                                                             (const uint16_t*)Q, o.gate, o.walk, o.temperature,
+                                                             o.uniforms,
                                                              path, path_score, path_idx, d.B, d.K, d.r, d.V);
         return hipGetLastError();
     }

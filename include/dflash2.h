@@ -216,9 +216,10 @@ typedef enum {
  *  uniforms    DFS_WALK_SAMPLE: [batch, B] fp32 device (else DFS_ERR_NULL):
  *              uniforms[b, t] in [0, 1) draws slot t of block b; column 0 is
  *              not read.  The library draws no random numbers itself.
- * Gated calls, and fp32 tables, K > 16 or r % 32 != 0, run the general
- * selector kernels (fp32 dot products); the others, with any walk, run one
- * fused kernel (MFMA dot products, fp32 accumulation).
+ * bf16 tables with K <= 16 and r % 32 == 0 run one fused kernel (MFMA dot
+ * products, fp32 accumulation; a gate enters as P (*) H formed in fp32 and
+ * split into two bf16 parts); fp32 tables, K > 16 or other ranks run the
+ * general selector kernels (fp32 dot products).
  */
 typedef struct {
     const float* gate;
@@ -274,7 +275,12 @@ DFS_API int dfs_select(const dfs_config* cfg, const dfs_select_opts* opts,
  * section "lightweight path selector": scoring is parallel over all slots,
  * and the walk is the only sequential part).
  * cand_ids / cand_logp are optional outputs (NULL: kept in the workspace).
- * Arguments as above.
+ * Arguments as above.  Small shapes, where the work is too little to cover
+ * the launches (block <= 16, K <= 16, hidden <= 512, vocab <= 1024 with
+ * vocab x hidden <= 2^17 and block x vocab <= 2^14, rank <= 512), run every
+ * step in one launch, one
+ * workgroup per block; their results match the three calls within the
+ * stated tolerances (the sums run in another order), with the same ids.
  */
 DFS_API int dfs_draft_block(const dfs_config* cfg, const dfs_select_opts* opts,
                     const void* h, const int32_t* anchor,
