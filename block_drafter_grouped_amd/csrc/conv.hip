@@ -168,6 +168,110 @@ __global__ __launch_bounds__(256) void conv_apply_kernel(const uint16_t* __restr
     }
 }
 
+// Few rows (at most kConvRowsMax, bf16): the whole conv in one launch, no
+// workspace.  One workgroup per (channel group, layer) computes the group's
+// ks tap logits over the full D for every row, their softmax, and the causal
+// taps of the group's gs channels.  Thread t takes 8-channel chunks t, t +
+// NT, ... of the generator rows and of every hidden row (all the loads of a
+// chunk in flight together, addresses clamped), the partial sums are reduced
+// across each wave in a fixed order and across the waves in order.  The
+// hidden rows are read once per group from L2; at 8 rows of the page shape
+// that is 320 workgroups of 100 KB each, against two launches and a round
+// trip of partials through the workspace for the split-D generator below.
+constexpr int kConvRowsMax = 16;
+
+// MR, MK: compile-time bounds of the rows and taps (8 and 2 for the page
+// shape at batch 1; 16 and 4 otherwise); NT threads.  With 256 threads
+// every workgroup of the page shape (320) is resident at once; 1024 threads
+// took 11.0 us against 7.1 us there (two rounds of workgroups).
+template <int MR, int MK, int NT>
+__global__ __launch_bounds__(NT) void conv_rows_kernel(const uint16_t* __restrict__ h,
+                                                        const uint16_t* __restrict__ wg, uint16_t* __restrict__ y,
+                                                        float* __restrict__ y_f32, int rows, int B, int D, int gs,
+                                                        int ks, int C) {
+    __shared__ float part[NT / kWave][MR][MK];  // [wave][row][tap]
+    __shared__ float wts[MR][MK];      // tap weights
+    const int g = blockIdx.x;
+    {  // grid y = layer
+        const size_t l = blockIdx.y;
+        h += l * rows * D;
+        wg += l * C * D;
+        y += l * rows * D;
+        if (y_f32) y_f32 += l * rows * D;
+    }
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    float acc[MR][MK];
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int j = 0; j < MK; ++j) acc[r][j] = 0.f;
+    const int nchunk = D / 8;
+    for (int ch = tid; ch < nchunk; ch += NT) {
+        float w8[MK][8], h8[MR][8];
+#pragma unroll
+        for (int j = 0; j < MK; ++j) {
+            const uint4 v = *(const uint4*)(wg + (size_t)(g * ks + min(j, ks - 1)) * D + 8 * ch);
+            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w8[j][2 * e] = __uint_as_float(q[e] << 16);
+                w8[j][2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const uint4 v = *(const uint4*)(h + (size_t)min(r, rows - 1) * D + 8 * ch);
+            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h8[r][2 * e] = __uint_as_float(q[e] << 16);
+                h8[r][2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int j = 0; j < MK; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[r][j] += h8[r][e] * w8[j][e];
+    }
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+#pragma unroll
+        for (int j = 0; j < MK; ++j) {
+            if (r < rows && j < ks) {  // uniform
+                const float sm = wave_sum_f32(acc[r][j]);
+                if (lane == 0) part[wave][r][j] = sm;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < rows) {  // tap logits in wave order, then the softmax over the taps
+        const int r = tid;
+        float z[MK], m = -INFINITY;
+        for (int j = 0; j < ks; ++j) {
+            z[j] = part[0][r][j];
+            for (int w = 1; w < NT / kWave; ++w) z[j] += part[w][r][j];
+            m = fmaxf(m, z[j]);
+        }
+        float ex[MK], den = 0.f;
+        for (int j = 0; j < ks; ++j) {
+            ex[j] = expf(z[j] - m);
+            den += ex[j];
+        }
+        for (int j = 0; j < ks; ++j) wts[r][j] = ex[j] / den;
+    }
+    __syncthreads();
+    for (int e = tid; e < rows * gs; e += NT) {  // causal taps, zero before the block
+        const int r = e / gs, c = g * gs + e % gs, t = r % B;
+        float v = 0.f;
+        for (int j = 0; j < ks; ++j)
+            if (t - j >= 0) v += wts[r][j] * bf16_to_f32(h[(size_t)(r - j) * D + c]);
+        y[(size_t)r * D + c] = f32_to_bf16(v);
+        if (y_f32) y_f32[(size_t)r * D + c] = v;
+    }
+}
+
 // fp32 correctness path: one workgroup per row.
 __global__ __launch_bounds__(256) void conv_f32_kernel(const float* __restrict__ h, const float* __restrict__ wg,
                                                        float* __restrict__ y, float* __restrict__ y_f32, int rows,
@@ -208,7 +312,8 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const float* __restrict__
 }  // namespace
 
 size_t conv_ws_bytes(const Dims& d) {
-    return d.bf16 ? (size_t)kConvSplit * d.rows() * d.taps() * sizeof(float) : 0;
+    // only the split-D generator (bf16, more than kConvRowsMax rows) keeps partials
+    return d.bf16 && d.rows() > kConvRowsMax ? (size_t)kConvSplit * d.rows() * d.taps() * sizeof(float) : 0;
 }
 
 hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y, float* y_f32, char* ws,
@@ -218,6 +323,17 @@ hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y,
         // One tap: the tap softmax is 1, so y = h (already in the dtype).
         return hipMemcpyAsync(y, h, (size_t)layers * d.rows() * d.D * (d.bf16 ? 2 : 4), hipMemcpyDeviceToDevice,
                               s);
+    }
+    if (d.bf16 && d.rows() <= kConvRowsMax) {
+        const dim3 grid(d.groups(), layers);
+        if (d.rows() <= 8 && d.ks <= 2)
+            conv_rows_kernel<8, 2, 256><<<grid, 256, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
+                                                            (uint16_t*)y, y_f32, d.rows(), d.B, d.D, d.gs, d.ks, C);
+        else
+            conv_rows_kernel<kConvRowsMax, 4, 256><<<grid, 256, 0, s>>>((const uint16_t*)h,
+                                                                       (const uint16_t*)wg_cm, (uint16_t*)y, y_f32,
+                                                                       d.rows(), d.B, d.D, d.gs, d.ks, C);
+        return hipGetLastError();
     }
     if (d.bf16) {
         float* zpart = (float*)(ws + ws_layout(d).zpart);

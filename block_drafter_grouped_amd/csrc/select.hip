@@ -308,86 +308,6 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const int32_t* __res
     if (tid == 0) path_score[b] = score_s;
 }
 
-// Transition tiles of one block on MFMA, from candidates already in LDS:
-// Cs[t][k] (ids) for t = 1..B-1, a valid anchor, and a barrier between
-// filling them and this call.  Every thread of the workgroup calls it.  Wave
-// w computes T_t for t = 1 + w, 1 + w + NWS, ... as one 16x16 MFMA tile
-// (A = P rows of the previous slot's candidates, or of the anchor for t = 1;
-// B = Q rows of this slot's candidates), with every gather of a slot in
-// flight at once.  With a context gate (row gate_rows + t * r of slot t) the
-// A operand is P (*) H, formed in fp32 and split into bf16 hi + lo parts that
-// take one MFMA each, so the product keeps about 16 significant bits beyond
-// bf16 (the rounding of the split is 2^-17 relative).
-template <int NWS>
-__device__ __forceinline__ void transition_tiles_mfma(int a, const int32_t (*Cs)[16], float (*Ts)[16][16],
-                                                      const uint16_t* __restrict__ P,
-                                                      const uint16_t* __restrict__ Q,
-                                                      const float* __restrict__ gate_rows, int B, int K, int r) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int i16 = lane & 15, q = lane >> 4, kk = min(i16, K - 1);
-    const int nks = r / 32;
-    for (int t = 1 + wave; t < B; t += NWS) {
-        const int pa = (t == 1) ? a : Cs[t - 1][kk];
-        const int qb = Cs[t][kk];
-        const uint16_t* pr = P + (size_t)pa * r + 8 * q;
-        const uint16_t* qr = Q + (size_t)qb * r + 8 * q;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (!gate_rows) {
-            for (int s0 = 0; s0 < nks; s0 += 8) {
-                bf16x8 av[8], bv[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int s = min(s0 + u, nks - 1);
-                    av[u] = *(const bf16x8*)(pr + 32 * s);
-                    bv[u] = *(const bf16x8*)(qr + 32 * s);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (s0 + u < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
-            }
-        } else {
-            const float* gr = gate_rows + (size_t)t * r + 8 * q;
-            for (int s0 = 0; s0 < nks; s0 += 4) {
-                uint4 pv[4];
-                bf16x8 bv[4];
-                f32x4 g0[4], g1[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int s = min(s0 + u, nks - 1);
-                    pv[u] = *(const uint4*)(pr + 32 * s);
-                    bv[u] = *(const bf16x8*)(qr + 32 * s);
-                    g0[u] = *(const f32x4*)(gr + 32 * s);
-                    g1[u] = *(const f32x4*)(gr + 32 * s + 4);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    if (s0 + u >= nks) continue;
-                    const uint32_t w4[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
-                    uint16_t hi[8], lo[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t bits = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
-                        const float x = __uint_as_float(bits) * (e < 4 ? g0[u][e] : g1[u][e - 4]);
-                        hi[e] = f32_to_bf16(x);
-                        lo[e] = f32_to_bf16(x - bf16_to_f32(hi[e]));
-                    }
-                    bf16x8 ah, al;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        ah[e] = __builtin_bit_cast(__bf16, hi[e]);
-                        al[e] = __builtin_bit_cast(__bf16, lo[e]);
-                    }
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv[u], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv[u], acc, 0, 0, 0);
-                }
-            }
-        }
-        // lane holds T_t[4q + rr][i16]
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) Ts[t - 1][4 * q + rr][i16] = acc[rr];
-    }
-}
-
 // Selector for bf16 tables with K <= 16 and r % 32 == 0, with or without a
 // context gate, on given candidates; any walk (mode 0: best path, 1: greedy,
 // 2: sampled).
@@ -395,34 +315,15 @@ template <int NWS>
 __global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
     const int32_t* __restrict__ anchor, const int32_t* __restrict__ cand_ids, const float* __restrict__ cand_logp,
     const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, const float* __restrict__ gate, int mode,
-    float temperature,
-    const float* __restrict__ uniforms, int32_t* __restrict__ path, float* __restrict__ path_score,
+    float temperature, const float* __restrict__ uniforms, int32_t* __restrict__ path, float* __restrict__ path_score,
     int32_t* __restrict__ path_idx, int B, int K, int r, int V) {
     extern __shared__ float Tsm[];  // [B-1][16][16]
     __shared__ float Ls[64][16];
     __shared__ float Us[64];
     __shared__ int32_t Cs[64][16];
     __shared__ uint8_t bp[64][16];
-    const int b = blockIdx.x, t0 = threadIdx.x;
-    const int a = anchor[b];
-    bool bad = (a < 0 || a >= V);
-    for (int i = t0; i < (B - 1) * K; i += NWS * kWave) {
-        const int t = 1 + i / K, k = i % K;
-        const int id = cand_ids[((size_t)b * B + t) * K + k];
-        bad |= (id < 0 || id >= V);
-        Cs[t][k] = id;
-        Ls[t][k] = cand_logp[((size_t)b * B + t) * K + k];
-    }
-    if (mode == 2)
-        for (int t = t0; t < B; t += NWS * kWave) Us[t] = uniforms[(size_t)b * B + t];
-    if (__syncthreads_or(bad)) {
-        write_bad_block(b, B, path, path_score, path_idx);
-        return;
-    }
-    float(*Ts)[16][16] = (float(*)[16][16])Tsm;
-    transition_tiles_mfma<NWS>(a, Cs, Ts, P, Q, gate ? gate + (size_t)b * B * r : nullptr, B, K, r);
-    __syncthreads();
-    walk_block_lds(b, a, Cs, Ls, Ts, bp, mode, 1.f / temperature, Us, path, path_score, path_idx, B, K);
+    select_block<NWS>(blockIdx.x, anchor, cand_ids, cand_logp, P, Q, gate, mode, temperature, uniforms, path,
+                      path_score, path_idx, B, K, r, V, Cs, Ls, (float(*)[16][16])Tsm, bp, Us);
 }
 
 }  // namespace

@@ -1,5 +1,7 @@
-// The walk of one block over transition tiles held in LDS (K <= 16), shared
-// by the fused selector and the single-launch block kernel.  Inco AI post
+// The selector of one block from LDS (K <= 16): transition tiles on MFMA and
+// the walk over them, shared by the selector kernels, the merge that runs
+// the selector of a block once its last row is ranked, and the single-launch
+// block kernel.  Inco AI post
 // "DFlash 2: keep the draft parallel", section "lightweight path selector":
 // every adjacent candidate pair is scored first; the only sequential work is
 // the walk over those scores, from the last verified token (vLLM
@@ -121,5 +123,122 @@ __device__ __forceinline__ void walk_block_lds(int b, int a, const int32_t (*Cs)
     }
 }
 
+
+// Transition tiles of one block on MFMA, from candidates already in LDS:
+// Cs[t][k] (ids) for t = 1..B-1, a valid anchor, and a barrier between
+// filling them and this call.  Every thread of the workgroup calls it.  Wave
+// w computes T_t for t = 1 + w, 1 + w + NWS, ... as one 16x16 MFMA tile
+// (A = P rows of the previous slot's candidates, or of the anchor for t = 1;
+// B = Q rows of this slot's candidates), with every gather of a slot in
+// flight at once.  With a context gate (row gate_rows + t * r of slot t) the
+// A operand is P (*) H, formed in fp32 and split into bf16 hi + lo parts that
+// take one MFMA each, so the product keeps about 16 significant bits beyond
+// bf16 (the rounding of the split is 2^-17 relative).
+template <int NWS>
+__device__ __forceinline__ void transition_tiles_mfma(int a, const int32_t (*Cs)[16], float (*Ts)[16][16],
+                                                      const uint16_t* __restrict__ P,
+                                                      const uint16_t* __restrict__ Q,
+                                                      const float* __restrict__ gate_rows, int B, int K, int r) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int i16 = lane & 15, q = lane >> 4, kk = min(i16, K - 1);
+    const int nks = r / 32;
+    for (int t = 1 + wave; t < B; t += NWS) {
+        const int pa = (t == 1) ? a : Cs[t - 1][kk];
+        const int qb = Cs[t][kk];
+        const uint16_t* pr = P + (size_t)pa * r + 8 * q;
+        const uint16_t* qr = Q + (size_t)qb * r + 8 * q;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (!gate_rows) {
+            for (int s0 = 0; s0 < nks; s0 += 8) {
+                bf16x8 av[8], bv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int s = min(s0 + u, nks - 1);
+                    av[u] = *(const bf16x8*)(pr + 32 * s);
+                    bv[u] = *(const bf16x8*)(qr + 32 * s);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
+            }
+        } else {
+            const float* gr = gate_rows + (size_t)t * r + 8 * q;
+            for (int s0 = 0; s0 < nks; s0 += 4) {
+                uint4 pv[4];
+                bf16x8 bv[4];
+                f32x4 g0[4], g1[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int s = min(s0 + u, nks - 1);
+                    pv[u] = *(const uint4*)(pr + 32 * s);
+                    bv[u] = *(const bf16x8*)(qr + 32 * s);
+                    g0[u] = *(const f32x4*)(gr + 32 * s);
+                    g1[u] = *(const f32x4*)(gr + 32 * s + 4);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (s0 + u >= nks) continue;
+                    const uint32_t w4[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+                    uint16_t hi[8], lo[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t bits = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
+                        const float x = __uint_as_float(bits) * (e < 4 ? g0[u][e] : g1[u][e - 4]);
+                        hi[e] = f32_to_bf16(x);
+                        lo[e] = f32_to_bf16(x - bf16_to_f32(hi[e]));
+                    }
+                    bf16x8 ah, al;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        ah[e] = __builtin_bit_cast(__bf16, hi[e]);
+                        al[e] = __builtin_bit_cast(__bf16, lo[e]);
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv[u], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv[u], acc, 0, 0, 0);
+                }
+            }
+        }
+        // lane holds T_t[4q + rr][i16]
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) Ts[t - 1][4 * q + rr][i16] = acc[rr];
+    }
+}
+
+
+// The whole selector of block b (bf16 tables, K <= 16, r % 32 == 0): stages
+// the block's candidates (global cand_ids / cand_logp) and uniforms in LDS,
+// marks a block with an invalid anchor or id, computes the transition tiles
+// and walks.  Every thread of the workgroup calls it; Cs, Ls, bp hold at
+// least B rows, Ts at least B - 1 tiles, Us B entries.
+template <int NWS>
+__device__ __forceinline__ void select_block(int b, const int32_t* __restrict__ anchor,
+                                             const int32_t* __restrict__ cand_ids,
+                                             const float* __restrict__ cand_logp, const uint16_t* __restrict__ P,
+                                             const uint16_t* __restrict__ Q, const float* __restrict__ gate, int mode,
+                                             float temperature, const float* __restrict__ uniforms,
+                                             int32_t* __restrict__ path, float* __restrict__ path_score,
+                                             int32_t* __restrict__ path_idx, int B, int K, int r, int V,
+                                             int32_t (*Cs)[16], float (*Ls)[16], float (*Ts)[16][16],
+                                             uint8_t (*bp)[16], float* Us) {
+    const int t0 = threadIdx.x;
+    const int a = anchor[b];
+    bool bad = (a < 0 || a >= V);
+    for (int i = t0; i < (B - 1) * K; i += NWS * kWave) {
+        const int t = 1 + i / K, k = i % K;
+        const int id = cand_ids[((size_t)b * B + t) * K + k];
+        bad |= (id < 0 || id >= V);
+        Cs[t][k] = id;
+        Ls[t][k] = cand_logp[((size_t)b * B + t) * K + k];
+    }
+    if (mode == 2)
+        for (int t = t0; t < B; t += NWS * kWave) Us[t] = uniforms[(size_t)b * B + t];
+    if (__syncthreads_or(bad)) {
+        write_bad_block(b, B, path, path_score, path_idx);
+        return;
+    }
+    transition_tiles_mfma<NWS>(a, Cs, Ts, P, Q, gate ? gate + (size_t)b * B * r : nullptr, B, K, r);
+    __syncthreads();
+    walk_block_lds(b, a, Cs, Ls, Ts, bp, mode, 1.f / temperature, Us, path, path_score, path_idx, B, K);
+}
 
 }  // namespace dfs
