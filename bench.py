@@ -220,9 +220,13 @@ def workload_line(wid: int, inp: dict, steps: int, cpu_calls: int, cpu_blocks=No
     us_step = timed(step, steps)
     dfs.conv(cfg, d["h"], wg_cm, y, ws)
     us_head = timed(lambda: dfs.head_topk(cfg, y, d["W"], ids, lp, lse, ws), steps)
+    gate = (0.5 + torch.rand((s.rows, s.rank), generator=torch.Generator().manual_seed(7))).cuda()
+    us_sel = timed(lambda: dfs.select(cfg, d["anchor"], ids, lp, d["P"], d["Q"], path, score, ws), steps)
+    us_sel_g = timed(lambda: dfs.select(cfg, d["anchor"], ids, lp, d["P"], d["Q"], path, score, ws, gate=gate), steps)
     out = {"workload": WORKLOAD_NAMES[wid], "steps": steps, "us_per_block": round(us_step / s.batch, 3),
            "us_per_step": round(us_step, 2), "blocks_per_s": round(s.batch / (us_step * 1e-6), 1),
-           **head_roofline(s, us_head), "outside_head_us": round(us_step - us_head, 2)}
+           **head_roofline(s, us_head), "outside_head_us": round(us_step - us_head, 2),
+           "select_us": round(us_sel, 2), "select_gated_us": round(us_sel_g, 2)}
     if graph:
         ms_g = graph_replay_ms(step, stream, steps)
         out["graph"] = {"us_per_step": round(ms_g * 1e3, 2), "blocks_per_s": round(s.batch / (ms_g * 1e-3), 1),
@@ -332,6 +336,10 @@ def main() -> int:
         del hL, wgL, yL, wsL
     us_head = timed(lambda: dfs.head_topk(cfg, y, W, ids, lp, lse, ws, stream=stream))
     us_sel = timed(lambda: dfs.select(cfg, anchor, ids, lp, P, Q, path, score, ws, stream=stream))
+    # The selector with a context gate (the Inco AI post's H(h_t); random
+    # fp32 rows in [0.5, 1.5), since the pages give no form for it).
+    gate = (0.5 + torch.rand((s.rows, s.rank), generator=torch.Generator().manual_seed(7))).cuda()
+    us_sel_gated = timed(lambda: dfs.select(cfg, anchor, ids, lp, P, Q, path, score, ws, stream=stream, gate=gate))
     vs = s.vocab // 8
     if not args.no_extras:
         # One GPU's share under vocabulary sharding over 8 GPUs: the head +
@@ -400,7 +408,8 @@ def main() -> int:
                    "hidden": s.hidden, "vocab": s.vocab, "top_k": s.top_k, "rank": s.rank,
                    "conv_group_size": s.group, "conv_kernel_size": s.ksize, "parallelism": "none (1 GPU)"},
         "us_per_block": round(ms_step * 1e3 / s.batch, 3),
-        "stage_us": {"conv": round(us_conv, 2), "head_topk": round(us_head, 2), "select": round(us_sel, 2)},
+        "stage_us": {"conv": round(us_conv, 2), "head_topk": round(us_head, 2), "select": round(us_sel, 2),
+                     "select_gated": round(us_sel_gated, 2)},
         "conv_layers_us": None if us_layers is None else
         {"layers": NL, "one_call": round(us_layers, 2), "separate_calls": round(us_separate, 2)},
         "vocab_shard_of_8": None if us_shard is None else
