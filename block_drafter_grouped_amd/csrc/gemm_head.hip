@@ -86,6 +86,30 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 #pragma clang diagnostic pop
 }
 
+// The same copy from a wave-uniform base address (an SGPR pair) plus a
+// per-lane byte offset: lane L reads sbase + voff and writes lds_base +
+// 16 L.  The address arithmetic stays on the scalar unit.  Address math on
+// the vector ALU (a 64-bit multiply-add per load) competes with the MFMA
+// waves of the same SIMD for issue: in a probe beside 8 MFMA waves, loaders
+// with vector-ALU addresses took 850 us for a stream that loaders with
+// scalar addresses finished in 529 us (the MFMA work alone took 509 us).
+template <bool STREAM>
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(
+                         __builtin_amdgcn_readfirstlane(lds_base)),
+                     "v"(voff), "s"(sbase)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
+                         __builtin_amdgcn_readfirstlane(lds_base)),
+                     "v"(voff), "s"(sbase)
+                     : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // The weight is read once, so its loads are non-temporal (they do not push
 // the reused hidden rows out of L2), except with 32-channel stages: there a
 // stage reads half of each 128-B weight line and the next stage the other
@@ -188,6 +212,15 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
         // L % UPR, i.e. logical unit (L % UPR) ^ f(row).
         const bool wl = wave < NWB + 2;
         const int pw = wl ? wave - NWB : wave - NWB - 2;
+        // Byte offset of lane L within a load instruction whose RPI rows are
+        // all in bounds: row L / UPR of the instruction, logical unit
+        // (L % UPR) ^ f(row).  f of tile row RPI n + r depends on n only
+        // through its parity (KC 64: f = (4 n + r / 2) & 7 with RPI 8; KC 32:
+        // f = (r / 4) & 3 with RPI 16), and a producer's instructions n = pw,
+        // pw + 2, ... share one parity, so one offset serves all of them, for
+        // W and for the hidden rows alike (both have rows of D elements).
+        const int lr = lane / UPR;
+        const uint32_t voff = (uint32_t)(lr * D * 2 + 16 * ((lane % UPR) ^ gemm_swz<KC>(RPI * (pw & 1) + lr)));
         // W load instructions of this producer in stage g: instruction n
         // covers tile rows RPI n .. RPI n + RPI - 1 and is skipped when all of
         // them lie past the range (the last tile of the range).
@@ -202,14 +235,30 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
             const int k0 = (g % S) * KC, v0 = v_beg + (g / S) * TV;
             const int nv = min(TV, v_end - v0);
             const uint32_t base = smem_base + (uint32_t)((g % RW) * WBYTES);
+            // Instruction n = pw + 2 i.  All address arithmetic is scalar.  A
+            // full tile issues straight-line code (a wave stalls on each
+            // taken branch); in the last tile of a range n grows with i, so
+            // the first instruction past the range ends the stage.
+            const uint16_t* wp = W + ((size_t)v0 + RPI * pw) * D + k0;
+            if (nv == TV) {
 #pragma unroll
-            for (int i = 0; i < WI; ++i) {
+                for (int i = 0; i < WI; ++i, wp += (size_t)2 * RPI * D)
+                    dma16s<kGemmStreamW<KC>>(wp, voff, base + (pw + 2 * i) * 1024);
+                return;
+            }
+#pragma unroll 1
+            for (int i = 0; i < WI; ++i, wp += (size_t)2 * RPI * D) {
                 const int n = pw + 2 * i;
-                if (RPI * n >= nv) continue;  // wave-uniform
-                const int vr = RPI * n + lane / UPR;
-                const int u = (lane % UPR) ^ gemm_swz<KC>(vr);
-                const int v = min(v0 + vr, v_end - 1);  // past the range: re-read its last row (cache hit)
-                dma16<kGemmStreamW<KC>>(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
+                if (RPI * n >= nv) break;  // wave-uniform
+                if (RPI * (n + 1) <= nv) {
+                    dma16s<kGemmStreamW<KC>>(wp, voff, base + n * 1024);
+                } else {
+                    // the one instruction across the end of the vocabulary
+                    const int vr = RPI * n + lane / UPR;
+                    const int u = (lane % UPR) ^ gemm_swz<KC>(vr);
+                    const int v = min(v0 + vr, v_end - 1);  // past the range: re-read its last row (cache hit)
+                    dma16<kGemmStreamW<KC>>(W + (size_t)v * D + k0 + 8 * u, base + n * 1024);
+                }
             }
         };
         // Hidden-row load instructions of this producer per stage: with RS
@@ -225,14 +274,26 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
         auto issue_y = [&](int g) {
             const int k0 = (g % S) * KC;
             const uint32_t base = ybase + (uint32_t)((g % RY) * YBYTES);
+            const uint16_t* yp = y + ((size_t)row_base + RPI * pw) * D + k0;
+            if (!RS || ny >= RP) {
 #pragma unroll
-            for (int i = 0; i < YI; ++i) {
+                for (int i = 0; i < YI; ++i, yp += (size_t)2 * RPI * D)
+                    dma16s<false>(yp, voff, base + (pw + 2 * i) * 1024);
+                return;
+            }
+#pragma unroll 1
+            for (int i = 0; i < YI; ++i, yp += (size_t)2 * RPI * D) {
                 const int n = pw + 2 * i;
-                if (RS && RPI * n >= ny) continue;  // wave-uniform
-                const int r = RPI * n + lane / UPR;
-                const int u = (lane % UPR) ^ gemm_swz<KC>(r);
-                const int row = min(row_base + r, rows_total - 1);
-                dma16<false>(y + (size_t)row * D + k0 + 8 * u, base + n * 1024);
+                if (RS && RPI * n >= ny) break;  // wave-uniform
+                if (!RS || RPI * (n + 1) <= ny) {
+                    dma16s<false>(yp, voff, base + n * 1024);
+                } else {
+                    // the one instruction across the last row
+                    const int r = RPI * n + lane / UPR;
+                    const int u = (lane % UPR) ^ gemm_swz<KC>(r);
+                    const int row = min(row_base + r, rows_total - 1);
+                    dma16<false>(y + (size_t)row * D + k0 + 8 * u, base + n * 1024);
+                }
             }
         };
         const int R = wl ? RW : RY;
@@ -281,34 +342,60 @@ __global__ __launch_bounds__((NWB + kGemmProducers) * kWave) void head_gemm_kern
             }
         }
     }
+    // LDS byte offsets of this lane's operand fragments (row block 0 and
+    // vocabulary block 0) at k-substep 0.  The stored unit of logical unit
+    // 2 ks + half is (half ^ f(row)) ^ 2 ks, so k-substep ks reads at the
+    // offset XOR 32 ks; rows 32 apart share f, so block b sits kBlk b bytes
+    // further.  Two registers then address every fragment of a stage.
+    constexpr uint32_t kBlk = 32 * KC * 2;
+    const uint32_t yo = 16u * (uint32_t)gemm_unit<KC>(rw * NRB * 32 + j, half);
+    const uint32_t wo = 16u * (uint32_t)gemm_unit<KC>(vw * NVB * 32 + j, half);
     int tile = 0, st = 0;
     for (int g = 0; g < total; ++g) {
         // vocabulary blocks of this wave that hold rows of the range (the
         // last tile of the range is partial); the others are skipped
         const int nvb = min(NVB, max(0, (v_end - (v_beg + tile * TV) - 32 * vw * NVB + 31) / 32));
         __syncthreads();  // stage g published
-        const uint4* sw = (const uint4*)(smem + (size_t)(g % RW) * WBYTES);
-        const uint4* sy = (const uint4*)(smem + (size_t)RW * WBYTES + (size_t)(g % RY) * YBYTES);
+        const uint8_t* sw = smem + (size_t)(g % RW) * WBYTES;
+        const uint8_t* sy = smem + (size_t)RW * WBYTES + (size_t)(g % RY) * YBYTES;
+        // Every MFMA of the stage runs, also for blocks past the end of the
+        // range in its last tile (or past the last hidden row): their rows
+        // hold copies of the last row or stale data, each output depends on
+        // its own weight row and hidden row only, and those results are
+        // dropped below.  Straight-line code lets the compiler issue the LDS
+        // reads of later fragments ahead of the MFMAs that use earlier ones;
+        // with a branch around each block every read waited for its data
+        // right before its MFMA.
+        // The stage's fragment reads form one sequence, q = ks NF + i: the
+        // NRB hidden-row fragments of k-substep ks, then its NVB weight
+        // fragments.  Each read is issued kAhead reads before the MFMAs of
+        // the weight fragment it runs level with, so the LDS latency hides
+        // behind earlier MFMAs (the scheduling barriers keep the compiler
+        // from sinking the reads back to their uses, which it does at this
+        // register budget).
+        constexpr int KS = KC / 16, NF = NRB + NVB, NQ = KS * NF, kAhead = 3;
+        bf16x8 F[NQ];
+        auto frag = [&](int q) {
+            const int ks = q / NF, i = q % NF;
+            const uint8_t* p = i < NRB ? sy + (yo ^ (32u * ks)) + kBlk * i : sw + (wo ^ (32u * ks)) + kBlk * (i - NRB);
+            return *(const bf16x8*)p;
+        };
+        int issued = 0;
 #pragma unroll
-        for (int ks = 0; ks < KC / 16; ++ks) {
-            const int u = 2 * ks + half;
-            bf16x8 bo[NRB];
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-                if (rb < nrb) bo[rb] = __builtin_bit_cast(bf16x8, sy[gemm_unit<KC>((rw * NRB + rb) * 32 + j, u)]);
-            // Rows past the range (and hidden rows past the last) hold
-            // copies of its last row, or stale data where their loads were
-            // skipped; each output depends on its own weight row and hidden
-            // row only, and those results are dropped below.
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
-                if (vb < nvb) {
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, sw[gemm_unit<KC>((vw * NVB + vb) * 32 + j, u)]);
+                const int qa = ks * NF + NRB + vb;
+                const int upto = min(qa + kAhead, NQ - 1);
 #pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb)
-                        if (rb < nrb)  // hidden rows as A, weight rows as B: see the store below
-                            acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[rb], a, acc[vb][rb], 0, 0, 0);
-                }
+                for (int q = 0; q < NQ; ++q)
+                    if (q >= issued && q <= upto) F[q] = frag(q);
+                issued = max(issued, upto + 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)  // hidden rows as A, weight rows as B: see the store below
+                    acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[ks * NF + rb], F[qa], acc[vb][rb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         if (st == S - 1) {

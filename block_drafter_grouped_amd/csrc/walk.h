@@ -1,7 +1,6 @@
 // The selector of one block from LDS (K <= 16): transition tiles on MFMA and
-// the walk over them, shared by the selector kernels, the merge that runs
-// the selector of a block once its last row is ranked, and the single-launch
-// block kernel.  Inco AI post
+// the walk over them, shared by the fused selector kernel and the
+// single-launch block kernel.  Inco AI post
 // "DFlash 2: keep the draft parallel", section "lightweight path selector":
 // every adjacent candidate pair is scored first; the only sequential work is
 // the walk over those scores, from the last verified token (vLLM
