@@ -108,38 +108,48 @@ def cpu_baseline(s, inp, budget_s: float) -> dict:
             "sample": f"{n} full call(s) of the same workload ({blocks} blocks) in {el:.1f} s; CPU: {cpu_model()}"}
 
 
-def graph_replay_ms(step, stream, steps: int, per_graph: int = 20) -> float:
-    """Milliseconds per step when ``per_graph`` steps are captured back to
-    back in one HIP graph and the graph is replayed until at least ``steps``
-    steps ran, timed on ``stream``.  With several steps per replay the
-    host's cost of issuing a replay is spread over them, so for shapes whose
-    GPU work is shorter than a host call this measures the GPU."""
+def graph_steps(step, stream, steps: int, per_graph: int = 20):
+    """Times exactly ``steps`` steps replayed from captured HIP graphs: one
+    graph of ``per_graph`` steps back to back replayed steps // per_graph
+    times, and one graph of the remaining steps.  Each graph is replayed
+    twice untimed first.  Several steps per replay spread the host's cost of
+    issuing a replay, so for shapes whose GPU work is shorter than a host call
+    this measures the GPU.  Returns (ms per step, wall seconds of the timed
+    region)."""
     import torch
 
+    full, rem = divmod(steps, per_graph)
     gstream = torch.cuda.Stream()
     gstream.wait_stream(stream)
     with torch.cuda.stream(gstream):
-        step(gstream)
+        step(gstream)  # once eagerly on the capture stream
     stream.wait_stream(gstream)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=gstream):
-        for _ in range(per_graph):
-            step(gstream)
+    graphs = []
+    for n in ([per_graph] if full else []) + ([rem] if rem else []):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            for _ in range(n):
+                step(gstream)
+        graphs.append(g)
     torch.cuda.synchronize()
-    for _ in range(2):
-        graph.replay()
+    for g in graphs:
+        g.replay()
+        g.replay()
     torch.cuda.synchronize()
-    reps = max(1, (steps + per_graph - 1) // per_graph)
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     g0.record(stream)
-    for _ in range(reps):
-        graph.replay()
+    for _ in range(full):
+        graphs[0].replay()
+    if rem:
+        graphs[-1].replay()
     g1.record(stream)
     torch.cuda.synchronize()
-    ms = g0.elapsed_time(g1) / (reps * per_graph)
-    del graph
-    return ms
+    wall = time.perf_counter() - t0
+    ms = g0.elapsed_time(g1) / steps
+    del graphs
+    return ms, wall
 
 
 def dev_tensor(a):
@@ -217,20 +227,20 @@ def workload_line(wid: int, inp: dict, steps: int, cpu_calls: int, cpu_blocks=No
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n * 1e3  # us
 
-    us_step = timed(step, steps)
+    us_eager = timed(step, steps)
+    us_step = graph_steps(step, stream, steps)[0] * 1e3 if graph else us_eager
     dfs.conv(cfg, d["h"], wg_cm, y, ws)
     us_head = timed(lambda: dfs.head_topk(cfg, y, d["W"], ids, lp, lse, ws), steps)
     gate = (0.5 + torch.rand((s.rows, s.rank), generator=torch.Generator().manual_seed(7))).cuda()
     us_sel = timed(lambda: dfs.select(cfg, d["anchor"], ids, lp, d["P"], d["Q"], path, score, ws), steps)
     us_sel_g = timed(lambda: dfs.select(cfg, d["anchor"], ids, lp, d["P"], d["Q"], path, score, ws, gate=gate), steps)
-    out = {"workload": WORKLOAD_NAMES[wid], "steps": steps, "us_per_block": round(us_step / s.batch, 3),
+    out = {"workload": WORKLOAD_NAMES[wid], "steps": steps,
+           "timing": "graph replay (20 steps per captured HIP graph)" if graph else "eager launches",
+           "us_per_block": round(us_step / s.batch, 3),
            "us_per_step": round(us_step, 2), "blocks_per_s": round(s.batch / (us_step * 1e-6), 1),
            **head_roofline(s, us_head), "outside_head_us": round(us_step - us_head, 2),
-           "select_us": round(us_sel, 2), "select_gated_us": round(us_sel_g, 2)}
-    if graph:
-        ms_g = graph_replay_ms(step, stream, steps)
-        out["graph"] = {"us_per_step": round(ms_g * 1e3, 2), "blocks_per_s": round(s.batch / (ms_g * 1e-3), 1),
-                        "note": "20 steps per captured HIP graph"}
+           "select_us": round(us_sel, 2), "select_gated_us": round(us_sel_g, 2),
+           "eager": {"us_per_step": round(us_eager, 2), "blocks_per_s": round(s.batch / (us_eager * 1e-6), 1)}}
     if cpu_calls > 0:
         out["cpu_baseline"] = cpu_sample(s, inp, cpu_calls, cpu_blocks)
     del d, wg_cm, ws
@@ -247,6 +257,8 @@ def main() -> int:
     ap.add_argument("--stage-steps", type=int, default=None, help="calls per stage timing loop")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run 4 plain 1 GiB device copies (counter calibration for profiles)")
+    ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
+                    help="time the K steps replayed from captured HIP graphs (default) or as eager launches")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the graph replay, per-layer conv and vocabulary-shard timings (for profiler runs: "
                          "their launches of the same kernels at other sizes would mix into per-kernel means)")
@@ -295,13 +307,17 @@ def main() -> int:
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
-
-    # The same step captured once in a HIP graph and replayed K times: the
+    wall_eager = time.perf_counter() - t0
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    # The headline: the same K steps replayed from captured HIP graphs (the
     # library takes the caller's stream and never allocates or synchronises,
-    # so a caller can cut the launch gaps this way.
-    ms_graph = None if args.no_extras else graph_replay_ms(step, stream, args.steps)
+    # so a serving loop can capture its draft step; the release-note article's
+    # cost section times the conv the same way).  --timing eager keeps eager
+    # launches (profiler runs).
+    if args.timing == "graph":
+        ms_step, wall = graph_steps(step, stream, args.steps)
+    else:
+        ms_step, wall = ms_eager, wall_eager
 
     # Per-stage split, each stage timed alone with HIP events on the same stream.
     n_stage = args.stage_steps or args.steps
@@ -350,20 +366,19 @@ def main() -> int:
         us_shard = timed(lambda: dfs.head_topk(cfg8, y, W[:vs], ids, lp, lse, ws8, stream=stream))
         del ws8
 
-    # The other workloads, each on its own seeded inputs: µs per block, the
-    # head stage against both roofs, the step replayed from a HIP graph for
-    # the launch-bound shapes, and a short oracle sample.
+    # The other workloads, each on its own seeded inputs: µs per block (timed
+    # as the headline is), the head stage against both roofs, and a short
+    # oracle sample.
     others = None
     if not args.no_extras:
         others = {}
-        plan = {0: (500, 5, None, True), 1: (200, 5, None, True), 3: (30, 1, [0, 1], False),
-                4: (30, 1, [0], False)}
-        for wid, (n, calls, blocks, with_graph) in plan.items():
+        plan = {0: (500, 5, None), 1: (200, 5, None), 3: (40, 1, [0, 1]), 4: (40, 1, [0])}
+        for wid, (n, calls, blocks) in plan.items():
             if wid == args.workload:
                 continue
             winp = wl.make_inputs(wid)
             others[str(wid)] = workload_line(wid, winp, n, calls if args.cpu_seconds > 0 else 0, blocks,
-                                             graph=with_graph)
+                                             graph=args.timing == "graph")
             del winp
 
     hb = head_stage_bytes(s)
@@ -419,9 +434,10 @@ def main() -> int:
         "block_hbm_frac": round(block_bytes(s) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "head_mfma_frac": round(head_flops(s) / (us_head * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
-        "graph": None if ms_graph is None else
-        {"ms_per_step": round(ms_graph, 5), "value": round(s.batch / (ms_graph * 1e-3), 2),
-         "note": "20 steps captured back to back in one HIP graph, replayed"},
+        "timing": "graph replay: the K steps captured 20 to a HIP graph, replayed; eager launches below"
+        if args.timing == "graph" else "eager launches",
+        "eager": {"ms_per_step": round(ms_eager, 5), "value": round(s.batch / (ms_eager * 1e-3), 2),
+                  "wall_s_timed": round(wall_eager, 3)},
         "workloads": others,
         "roofline": roof,
         "cpu_baseline": None,
