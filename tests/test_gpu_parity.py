@@ -474,7 +474,7 @@ def test_select_figure1_repetition():
 # ============================================================== selector options (gate, walks)
 
 GATE_SHAPES = [
-    S(batch=4, block=8, vocab=5000, top_k=16, rank=256),           # bf16, K 16: leaves the fused kernel
+    S(batch=4, block=8, vocab=5000, top_k=16, rank=256),           # bf16, K 16: the fused MFMA selector
     S(batch=3, block=5, vocab=4000, top_k=33, rank=8),             # general path
     S(batch=5, block=16, vocab=2000, top_k=16, rank=256, dtype="f32"),
 ]
