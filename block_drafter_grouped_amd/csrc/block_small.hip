@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kSmallThreads) void block_small_kernel(
     __shared__ int32_t Cs[kSmallMaxB][16];
     __shared__ float Ls[kSmallMaxB][16];
     __shared__ float Ts[kSmallMaxB - 1][16][16];
-    __shared__ uint8_t bp[kSmallMaxB][16];
+    __shared__ __attribute__((aligned(16))) uint8_t bp[kSmallMaxB][16];
     __shared__ float Us[kSmallMaxB];
     __shared__ __attribute__((aligned(16))) float ones8[8];  // the gate when there is none
     constexpr bool kBf16 = sizeof(T) == 2;

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(NWS * kWave) void select_fused_kernel(
     __shared__ float Ls[64][16];
     __shared__ float Us[64];
     __shared__ int32_t Cs[64][16];
-    __shared__ uint8_t bp[64][16];
+    __shared__ __attribute__((aligned(16))) uint8_t bp[64][16];
     select_block<NWS>(blockIdx.x, anchor, cand_ids, cand_logp, P, Q, gate, mode, temperature, uniforms, path,
                       path_score, path_idx, B, K, r, V, Cs, Ls, (float(*)[16][16])Tsm, bp, Us);
 }

@@ -75,51 +75,103 @@ __device__ __forceinline__ void walk_block_lds(int b, int a, const int32_t (*Cs)
     }
 
     // Lane 16 g + k: candidate k, predecessors j = 4g .. 4g + 3.  Each lane
-    // scans its four j (the first, then a strict comparison), then two
-    // butterfly steps combine the groups, the lower j winning ties: the
+    // scans its four j (the first, then a strict comparison); two butterfly
+    // steps then combine the four groups, the lower j winning ties: the
     // lowest j with the largest score, as a left-to-right scan finds it.
-    // delta[k] ends up in all four lanes of k; lane j (group 0) serves
-    // delta[j] to the next slot.
+    //  - delta reaches the lanes through 16 floats of LDS: lanes 0 .. 15
+    //    write delta[k], every lane reads its group's delta[4g .. 4g + 3]
+    //    with one 16-B broadcast read;
+    //  - the butterflies exchange across rows with v_permlane16_swap and
+    //    v_permlane32_swap, which give every lane both its own and its
+    //    partner's pair (a symmetric combine needs no more);
+    //  - the next slot's T and node scores are read while this slot's
+    //    scores are formed.
+    // (Shuffles through the LDS unit for all three exchanges cost about 1000
+    // cycles per slot; this walk takes a few hundred.)
+    __shared__ __attribute__((aligned(16))) float dsh[16];
     const int k = lane & 15, g = lane >> 4;
     const bool on = k < K;
+    auto pair_max = [](float& bv, int& bi, float ov, int oi) {
+        const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+        bv = take ? ov : bv;
+        bi = take ? oi : bi;
+    };
     float d = on ? Ls[1][k] + Ts[0][0][k] : -INFINITY;
+    float tn[4], ln = 0.f;
+    auto fetch = [&](int t) {  // T_t[4g + i][k] and the node score of slot t
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tn[i] = Ts[t - 1][4 * g + i][k];
+        ln = Ls[t][k];
+    };
+    if (B > 2) fetch(2);
     for (int t = 2; t < B; ++t) {
+        float tc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tc[i] = tn[i];
+        const float lc = ln;
+        if (lane < 16) dsh[lane] = d;
+        const f32x4 d4 = *(const f32x4*)&dsh[4 * g];
+        fetch(min(t + 1, B - 1));  // unconditional (the last slot re-reads itself): no wait for it here
         float bv = -INFINITY;
         int bi = 4 * g;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int j = 4 * g + i;
-            const float dj = __shfl(d, j, kWave);
-            const float c = (j < K) ? dj + Ts[t - 1][j][k] : -INFINITY;
+            const float c = (j < K) ? d4[i] + tc[i] : -INFINITY;
             const bool gt = (i == 0) | (c > bv);
             bv = gt ? c : bv;
             bi = gt ? j : bi;
         }
-#pragma unroll
-        for (int o = 16; o < kWave; o <<= 1) {
-            const float ov = __shfl_xor(bv, o, kWave);
-            const int oi = __shfl_xor(bi, o, kWave);
-            const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
-            bv = take ? ov : bv;
-            bi = take ? oi : bi;
+        {
+            const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+            const auto x = __builtin_amdgcn_permlane16_swap((uint32_t)bi, (uint32_t)bi, false, false);
+            bv = __uint_as_float(v[0]);
+            bi = (int)x[0];
+            pair_max(bv, bi, __uint_as_float(v[1]), (int)x[1]);
         }
-        d = on ? bv + Ls[t][k] : -INFINITY;
+        {
+            const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+            const auto x = __builtin_amdgcn_permlane32_swap((uint32_t)bi, (uint32_t)bi, false, false);
+            bv = __uint_as_float(v[0]);
+            bi = (int)x[0];
+            pair_max(bv, bi, __uint_as_float(v[1]), (int)x[1]);
+        }
+        d = on ? bv + lc : -INFINITY;
         if (on && g == 0) bp[t][k] = (uint8_t)bi;
     }
     const float mx = wave_max_f32(d);
     const uint64_t ball = __ballot(on && g == 0 && d == mx);
-    const int kb = __ffsll((unsigned long long)ball) - 1;
-    if (lane == 0) {
-        int k = kb;
-        for (int t = B - 1; t >= 1; --t) {
-            path[(size_t)b * B + t] = Cs[t][k];
-            if (path_idx) path_idx[(size_t)b * B + t] = k;
-            if (t >= 2) k = bp[t][k];
-        }
-        path[(size_t)b * B] = a;
-        if (path_idx) path_idx[(size_t)b * B] = -1;
-        path_score[b] = mx;
+    // Backtrack.  The back-pointer table (bytes bp[t][k], word 4 t + k / 4)
+    // goes to registers, four words per lane; the chase then runs on the
+    // scalar unit through v_readlane, and lane t keeps the index of slot t,
+    // so that every lane writes its own path element (no dependent LDS read
+    // per slot).
+    uint32_t bpw[4];
+    const int nw = 4 * B;  // words in use
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int w = lane + 64 * m;
+        bpw[m] = (m * 64 < nw) ? ((const uint32_t*)bp)[min(w, nw - 1)] : 0u;
     }
+    int kk = __ffsll((unsigned long long)ball) - 1;  // uniform
+    int kt = 0;                                     // lane t: the index of slot t
+    for (int t = B - 1; t >= 1; --t) {
+        kt = lane == t ? kk : kt;
+        if (t >= 2) {
+            const int w = 4 * t + (kk >> 2);
+            const int m = w >> 6, l = w & 63;
+            const uint32_t word = m == 0   ? (uint32_t)__builtin_amdgcn_readlane((int)bpw[0], l)
+                                  : m == 1 ? (uint32_t)__builtin_amdgcn_readlane((int)bpw[1], l)
+                                  : m == 2 ? (uint32_t)__builtin_amdgcn_readlane((int)bpw[2], l)
+                                           : (uint32_t)__builtin_amdgcn_readlane((int)bpw[3], l);
+            kk = (int)((word >> (8 * (kk & 3))) & 0xFFu);
+        }
+    }
+    if (lane < B) {
+        path[(size_t)b * B + lane] = lane == 0 ? a : Cs[lane][kt];
+        if (path_idx) path_idx[(size_t)b * B + lane] = lane == 0 ? -1 : kt;
+    }
+    if (lane == 0) path_score[b] = mx;
 }
 
 
