@@ -175,16 +175,75 @@ __device__ __forceinline__ void walk_block_lds(int b, int a, const int32_t (*Cs)
 }
 
 
+// One transition tile T_t (16 x 16, K <= 16) on MFMA, as one wave:
+// A = P rows (or P (*) H rows with a context gate) of the predecessors, B =
+// Q rows of the successors.  Lane 16 q + i holds predecessor row pr and
+// successor row qr of index i (both already offset by 8 q elements) and the
+// gate row gr (offset the same, or null); every gather of the tile is in
+// flight at once.  With a gate, P (*) H is formed in fp32 and split into
+// bf16 hi + lo parts that take one MFMA each, so the product keeps about 16
+// significant bits beyond bf16 (the rounding of the split is 2^-17
+// relative).  Returns the lane's part of the tile: T[4 q + rr][i], rr = 0..3.
+__device__ __forceinline__ f32x4 transition_tile_mfma(const uint16_t* __restrict__ pr, const uint16_t* __restrict__ qr,
+                                                      const float* __restrict__ gr, int nks) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (!gr) {
+        for (int s0 = 0; s0 < nks; s0 += 8) {
+            bf16x8 av[8], bv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = min(s0 + u, nks - 1);
+                av[u] = *(const bf16x8*)(pr + 32 * s);
+                bv[u] = *(const bf16x8*)(qr + 32 * s);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
+        }
+    } else {
+        for (int s0 = 0; s0 < nks; s0 += 4) {
+            uint4 pv[4];
+            bf16x8 bv[4];
+            f32x4 g0[4], g1[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int s = min(s0 + u, nks - 1);
+                pv[u] = *(const uint4*)(pr + 32 * s);
+                bv[u] = *(const bf16x8*)(qr + 32 * s);
+                g0[u] = *(const f32x4*)(gr + 32 * s);
+                g1[u] = *(const f32x4*)(gr + 32 * s + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (s0 + u >= nks) continue;
+                const uint32_t w4[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+                uint16_t hi[8], lo[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t bits = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
+                    const float x = __uint_as_float(bits) * (e < 4 ? g0[u][e] : g1[u][e - 4]);
+                    hi[e] = f32_to_bf16(x);
+                    lo[e] = f32_to_bf16(x - bf16_to_f32(hi[e]));
+                }
+                bf16x8 ah, al;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ah[e] = __builtin_bit_cast(__bf16, hi[e]);
+                    al[e] = __builtin_bit_cast(__bf16, lo[e]);
+                }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv[u], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv[u], acc, 0, 0, 0);
+            }
+        }
+    }
+    return acc;
+}
+
 // Transition tiles of one block on MFMA, from candidates already in LDS:
 // Cs[t][k] (ids) for t = 1..B-1, a valid anchor, and a barrier between
 // filling them and this call.  Every thread of the workgroup calls it.  Wave
-// w computes T_t for t = 1 + w, 1 + w + NWS, ... as one 16x16 MFMA tile
-// (A = P rows of the previous slot's candidates, or of the anchor for t = 1;
-// B = Q rows of this slot's candidates), with every gather of a slot in
-// flight at once.  With a context gate (row gate_rows + t * r of slot t) the
-// A operand is P (*) H, formed in fp32 and split into bf16 hi + lo parts that
-// take one MFMA each, so the product keeps about 16 significant bits beyond
-// bf16 (the rounding of the split is 2^-17 relative).
+// w computes T_t for t = 1 + w, 1 + w + NWS, ... into LDS (row gate_rows +
+// t * r of the gate goes with slot t).
 template <int NWS>
 __device__ __forceinline__ void transition_tiles_mfma(int a, const int32_t (*Cs)[16], float (*Ts)[16][16],
                                                       const uint16_t* __restrict__ P,
@@ -192,63 +251,11 @@ __device__ __forceinline__ void transition_tiles_mfma(int a, const int32_t (*Cs)
                                                       const float* __restrict__ gate_rows, int B, int K, int r) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int i16 = lane & 15, q = lane >> 4, kk = min(i16, K - 1);
-    const int nks = r / 32;
     for (int t = 1 + wave; t < B; t += NWS) {
         const int pa = (t == 1) ? a : Cs[t - 1][kk];
         const int qb = Cs[t][kk];
-        const uint16_t* pr = P + (size_t)pa * r + 8 * q;
-        const uint16_t* qr = Q + (size_t)qb * r + 8 * q;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (!gate_rows) {
-            for (int s0 = 0; s0 < nks; s0 += 8) {
-                bf16x8 av[8], bv[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int s = min(s0 + u, nks - 1);
-                    av[u] = *(const bf16x8*)(pr + 32 * s);
-                    bv[u] = *(const bf16x8*)(qr + 32 * s);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (s0 + u < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
-            }
-        } else {
-            const float* gr = gate_rows + (size_t)t * r + 8 * q;
-            for (int s0 = 0; s0 < nks; s0 += 4) {
-                uint4 pv[4];
-                bf16x8 bv[4];
-                f32x4 g0[4], g1[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int s = min(s0 + u, nks - 1);
-                    pv[u] = *(const uint4*)(pr + 32 * s);
-                    bv[u] = *(const bf16x8*)(qr + 32 * s);
-                    g0[u] = *(const f32x4*)(gr + 32 * s);
-                    g1[u] = *(const f32x4*)(gr + 32 * s + 4);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    if (s0 + u >= nks) continue;
-                    const uint32_t w4[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
-                    uint16_t hi[8], lo[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t bits = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
-                        const float x = __uint_as_float(bits) * (e < 4 ? g0[u][e] : g1[u][e - 4]);
-                        hi[e] = f32_to_bf16(x);
-                        lo[e] = f32_to_bf16(x - bf16_to_f32(hi[e]));
-                    }
-                    bf16x8 ah, al;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        ah[e] = __builtin_bit_cast(__bf16, hi[e]);
-                        al[e] = __builtin_bit_cast(__bf16, lo[e]);
-                    }
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv[u], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv[u], acc, 0, 0, 0);
-                }
-            }
-        }
+        const f32x4 acc = transition_tile_mfma(P + (size_t)pa * r + 8 * q, Q + (size_t)qb * r + 8 * q,
+                                               gate_rows ? gate_rows + (size_t)t * r + 8 * q : nullptr, r / 32);
         // lane holds T_t[4q + rr][i16]
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) Ts[t - 1][4 * q + rr][i16] = acc[rr];

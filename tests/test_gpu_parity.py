@@ -409,6 +409,9 @@ SELECT_SHAPES = [
     S(batch=2, block=64, vocab=3000, top_k=17, rank=40),
     S(batch=3, block=40, vocab=6000, top_k=48, rank=24, dtype="f32"),
     S(batch=2, block=4, vocab=5000, top_k=16, rank=4096),  # the largest rank
+    # the fused MFMA selector at the longest block: the walk's back-pointer
+    # table fills all four of its registers per lane
+    S(batch=2, block=64, vocab=9000, top_k=16, rank=64),
 ]
 
 
