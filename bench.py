@@ -260,7 +260,7 @@ def main() -> int:
     ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
                     help="time the K steps replayed from captured HIP graphs (default) or as eager launches")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the graph replay, per-layer conv and vocabulary-shard timings (for profiler runs: "
+                    help="skip the per-layer conv, vocabulary-shard and other-workload timings (for profiler runs: "
                          "their launches of the same kernels at other sizes would mix into per-kernel means)")
     args = ap.parse_args()
 

@@ -7,8 +7,9 @@
 // section "two additions").  The post's context gate H(h_t) is optional: the
 // caller supplies it, or it is 1.
 //
-// Fast path (bf16 tables, K <= 16, r % 32 == 0; any walk, with or without a
-// gate): select_fused_kernel, below.  General path:
+// Fast path (bf16 tables, K <= 16, r % 32 == 0, with or without a gate; the
+// best path at any block length, greedy and sampled walks up to 16 slots):
+// select_fused_kernel, below.  General path:
 // sel_dots: one workgroup per (draft slot, block, 16 x 16 sub-tile) computes
 // the K x K matrix
 //   T_t[j, k] = sum_i P[c_{t-1, j}, i] * H_t[i] * Q[c_{t, k}, i]

@@ -575,8 +575,8 @@ def check_walk(s, ids, lp, P, Q, anchor, pidx, score, walk, temperature=1.0, uni
 
 def random_select_cases(n, seed=2027):
     """Seeded selector cases: shape, walk rule, gate on or off; fused and
-    general kernels both get exercised (bf16, K <= 16, r % 32 == 0, no gate,
-    and B <= 16 for greedy and sampled walks, run the fused kernel)."""
+    general kernels both get exercised (bf16, K <= 16, r % 32 == 0, and B <=
+    16 for greedy and sampled walks, run the fused kernel, gated or not)."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
