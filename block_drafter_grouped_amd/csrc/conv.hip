@@ -23,8 +23,11 @@ namespace {
 // idle and be bound by per-CU bandwidth.  The D reduction is therefore split
 // over kConvSplit workgroups per tile, whose partial tiles go to the
 // workspace; a second kernel sums them in a fixed order, applies the tap
-// softmax and the causal taps.  (Eight splits measured slower at 256 rows.)
-constexpr int kConvSplit = 4;
+// softmax and the causal taps.  Six splits put the 40 tiles of the page
+// shape on 240 CUs: the conv took 14.6, 21.0 and 24.3 us at 64, 128 and 256
+// rows against 15.8, 23.0 and 26.6 us with four splits; seven and eight
+// (more workgroups than CUs) were slower at 64 and 256 rows.
+constexpr int kConvSplit = 6;
 constexpr int kConvNarrowRows = 64;
 constexpr int kGenWaves = 4;
 
