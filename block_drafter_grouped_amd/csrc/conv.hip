@@ -339,15 +339,8 @@ hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y,
         return hipGetLastError();
     }
     if (d.bf16) {
-        float* zpart = (float*)(ws + ws_layout(d).zpart);
-        if (d.rows() <= 16) {
-            // Few rows: 16 generator columns per workgroup, so that enough
-            // workgroups stream the generator.  Two k-steps in flight per
-            // wave (8 rows of the page shape: conv 10.5 -> 9.5 us against 8).
-            dim3 grid((C + 15) / 16, 1, kConvSplit * layers);
-            conv_gen_kernel<1, 1, 2><<<grid, kGenWaves * kWave, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
-                                                                       zpart, d.rows(), d.D, C);
-        } else if (d.rows() <= kConvNarrowRows) {
+        float* zpart = (float*)(ws + ws_layout(d).zpart);  // more than kConvRowsMax rows here
+        if (d.rows() <= kConvNarrowRows) {
             // Up to kConvNarrowRows rows: 16 columns x 64 rows, so that enough
             // workgroups still stream the generator (two k-steps in flight:
             // 40 rows, 16.6 -> 14.4 us).
