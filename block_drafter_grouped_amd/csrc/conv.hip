@@ -171,29 +171,96 @@ __global__ __launch_bounds__(256) void conv_apply_kernel(const uint16_t* __restr
     }
 }
 
+// Sums each of N values (N = 16 or 64) over the 64 lanes of a wave in one
+// transposed butterfly: every step halves the values a lane holds and
+// exchanges the other half with the partner lane, so N sums cost about N
+// exchanges instead of N full reductions.  The steps pair lanes across bit
+// 5 (v_permlane32_swap), bit 4 (v_permlane16_swap), then bits 3, 2, 1, 0
+// (DPP row mirror, half-row mirror, quad permutes); a pair is added in a
+// fixed order, so the result does not vary from run to run.  On return the
+// wave's sum of value o is in lane 4 o (N = 16; lanes 4 o .. 4 o + 3 hold
+// it) or lane o (N = 64).
+template <int N>
+__device__ __forceinline__ float wave_sum_transposed(const float (&v)[N]) {
+    static_assert(N == 16 || N == 64, "16 or 64 values");
+    const int lane = threadIdx.x & (kWave - 1);
+    float w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {  // lanes < 32 keep value i, lanes >= 32 value i + N/2
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 2]), false,
+                                                        false);
+        w[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    float u[N / 4];
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {  // even rows of 16 lanes keep value i, odd rows i + N/4
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[i]), __float_as_uint(w[i + N / 4]), false,
+                                                        false);
+        u[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    // A lane keeps the half its bit selects and sends the other half to the
+    // partner, whose bit is the opposite.
+    auto halve = [&](float a, float b, bool bit, auto dpp) {
+        const float send = bit ? a : b;
+        return (bit ? b : a) + dpp(send);
+    };
+    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+    const auto mir = [](float x) { return dpp_f32<kDppMirror>(x); };
+    const auto hmir = [](float x) { return dpp_f32<kDppHalfMirror>(x); };
+    const auto x2 = [](float x) { return dpp_f32<kDppQuadXor2>(x); };
+    const auto x1 = [](float x) { return dpp_f32<kDppQuadXor1>(x); };
+    if constexpr (N == 16) {
+        const float t0 = halve(u[0], u[2], b3, mir), t1 = halve(u[1], u[3], b3, mir);
+        float s = halve(t0, t1, b2, hmir);
+        s += x2(s);
+        return s + x1(s);
+    } else {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = halve(u[i], u[i + 8], b3, mir);
+        float q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = halve(t[i], t[i + 4], b2, hmir);
+        const float r0 = halve(q[0], q[2], b1, x2), r1 = halve(q[1], q[3], b1, x2);
+        return halve(r0, r1, b0, x1);
+    }
+}
+
 // Few rows (at most kConvRowsMax, bf16): the whole conv in one launch, no
 // workspace.  One workgroup per (channel group, layer) computes the group's
 // ks tap logits over the full D for every row, their softmax, and the causal
 // taps of the group's gs channels.  Thread t takes 8-channel chunks t, t +
-// NT, ... of the generator rows and of every hidden row (all the loads of a
-// chunk in flight together, addresses clamped), the partial sums are reduced
-// across each wave in a fixed order and across the waves in order.  The
-// hidden rows are read once per group from L2; at 8 rows of the page shape
-// that is 320 workgroups of 100 KB each, against two launches and a round
-// trip of partials through the workspace for the split-D generator below.
+// NT, ... of the generator rows and of every hidden row.  At 8 rows of the
+// page shape that is 320 workgroups, all resident at once, each reading the
+// hidden rows (80 KB, from L2) and its generator rows (20 KB).
+//
+// Timestamped at the page shape, the workgroup of an earlier form (256
+// threads, one chunk's loads at a time) was a chain of latencies: three
+// rounds of loads (2.7 us), sixteen wave reductions one after another (1.2
+// us), the softmax behind a barrier (0.5 us), then a round trip for the
+// causal taps' hidden values (0.6 us).  Here the loads of CPT chunks go out
+// together, the hidden values of the causal taps are loaded first (they do
+// not depend on the tap weights), the partial sums take one transposed wave
+// reduction, and each thread of the causal taps forms its row's softmax from
+// the wave partials, with no branch.  Measured per call (graph-replayed, 8
+// rows): 6.4 -> 4.9 us at D 5120 and 5.1 -> 3.6 us at D 2560 with 320
+// threads (two chunks per thread at D 5120, one at D 2560); 256 threads
+// with three chunks took 5.5 us at D 5120, 384 threads 5.7 us, 640 threads
+// 6.7 us, and two groups per workgroup (256 workgroups, no CU running two)
+// 5.9 us.  At 16 rows (256 threads, one chunk in flight): 12.3 -> 10.2 us
+// and 9.0 -> 6.3 us.
 constexpr int kConvRowsMax = 16;
 
 // MR, MK: compile-time bounds of the rows and taps (8 and 2 for the page
-// shape at batch 1; 16 and 4 otherwise); NT threads.  With 256 threads
-// every workgroup of the page shape (320) is resident at once; 1024 threads
-// took 11.0 us against 7.1 us there (two rounds of workgroups).
-template <int MR, int MK, int NT>
+// shape at batch 1; 16 and 4 otherwise); NT threads; CPT chunks per thread
+// in flight together.
+template <int MR, int MK, int NT, int CPT>
 __global__ __launch_bounds__(NT) void conv_rows_kernel(const uint16_t* __restrict__ h,
                                                         const uint16_t* __restrict__ wg, uint16_t* __restrict__ y,
                                                         float* __restrict__ y_f32, int rows, int B, int D, int gs,
                                                         int ks, int C) {
-    __shared__ float part[NT / kWave][MR][MK];  // [wave][row][tap]
-    __shared__ float wts[MR][MK];      // tap weights
+    constexpr int NWV = NT / kWave, NV = MR * MK;
+    __shared__ float part[NWV][NV];  // [wave][row * MK + tap]: each wave's sums
     const int g = blockIdx.x;
     {  // grid y = layer
         const size_t l = blockIdx.y;
@@ -203,75 +270,107 @@ __global__ __launch_bounds__(NT) void conv_rows_kernel(const uint16_t* __restric
         if (y_f32) y_f32 += l * rows * D;
     }
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    float acc[MR][MK];
+
+    // This thread's first causal-tap output (row r0, channel c0) and its
+    // hidden values (rows before the block are never used).
+    const int napply = rows * gs;
+    const int e0 = min(tid, napply - 1);
+    const int r0 = e0 / gs, c0 = g * gs + e0 % gs, t0 = r0 % B;
+    float hp[MK];
 #pragma unroll
-    for (int r = 0; r < MR; ++r)
+    for (int j = 0; j < MK; ++j) hp[j] = bf16_to_f32(h[(size_t)max(r0 - j, 0) * D + c0]);
+
+    const uint16_t* wrow[MK];
 #pragma unroll
-        for (int j = 0; j < MK; ++j) acc[r][j] = 0.f;
+    for (int j = 0; j < MK; ++j) wrow[j] = wg + (size_t)(g * ks + min(j, ks - 1)) * D;
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
     const int nchunk = D / 8;
-    for (int ch = tid; ch < nchunk; ch += NT) {
-        float w8[MK][8], h8[MR][8];
+    for (int cb = tid; cb < nchunk; cb += NT * CPT) {
+        uint4 wv[CPT][MK], hv[CPT][MR];
 #pragma unroll
-        for (int j = 0; j < MK; ++j) {
-            const uint4 v = *(const uint4*)(wg + (size_t)(g * ks + min(j, ks - 1)) * D + 8 * ch);
-            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+        for (int i = 0; i < CPT; ++i) {
+            const int ch = min(cb + NT * i, nchunk - 1);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                w8[j][2 * e] = __uint_as_float(q[e] << 16);
-                w8[j][2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
+            for (int j = 0; j < MK; ++j) wv[i][j] = *(const uint4*)(wrow[j] + 8 * ch);
+#pragma unroll
+            for (int r = 0; r < MR; ++r) hv[i][r] = *(const uint4*)(h + (size_t)min(r, rows - 1) * D + 8 * ch);
+        }
+        // Every load above is issued before the first is used: a chunk past
+        // the end (its address clamped) is zeroed instead of branched around,
+        // and the scheduler may not sink the loads below this point.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const bool live = cb + NT * i < nchunk;
+            float w8[MK][8];
+#pragma unroll
+            for (int j = 0; j < MK; ++j) {
+                const uint4 v = wv[i][j];
+                const uint32_t q[4] = {live ? v.x : 0u, live ? v.y : 0u, live ? v.z : 0u, live ? v.w : 0u};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w8[j][2 * e] = __uint_as_float(q[e] << 16);
+                    w8[j][2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const uint4 v = hv[i][r];
+                const uint32_t q[4] = {live ? v.x : 0u, live ? v.y : 0u, live ? v.z : 0u, live ? v.w : 0u};
+                float h8[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h8[2 * e] = __uint_as_float(q[e] << 16);
+                    h8[2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int j = 0; j < MK; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[r * MK + j] += h8[e] * w8[j][e];
             }
         }
-#pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            const uint4 v = *(const uint4*)(h + (size_t)min(r, rows - 1) * D + 8 * ch);
-            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h8[r][2 * e] = __uint_as_float(q[e] << 16);
-                h8[r][2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < MR; ++r)
-#pragma unroll
-            for (int j = 0; j < MK; ++j)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[r][j] += h8[r][e] * w8[j][e];
     }
-#pragma unroll
-    for (int r = 0; r < MR; ++r) {
-#pragma unroll
-        for (int j = 0; j < MK; ++j) {
-            if (r < rows && j < ks) {  // uniform
-                const float sm = wave_sum_f32(acc[r][j]);
-                if (lane == 0) part[wave][r][j] = sm;
-            }
-        }
+    {
+        const float sm = wave_sum_transposed<NV>(acc);
+        if ((lane & (kWave / NV - 1)) == 0) part[wave][lane / (kWave / NV)] = sm;
     }
     __syncthreads();
-    if (tid < rows) {  // tap logits in wave order, then the softmax over the taps
-        const int r = tid;
+    // Causal taps, zero before the block: the tap logits are the wave
+    // partials summed in wave order, then their softmax (taps past ks get
+    // weight 0).
+    auto tap = [&](int r, int c, int t, const float (&hv)[MK]) {
         float z[MK], m = -INFINITY;
-        for (int j = 0; j < ks; ++j) {
-            z[j] = part[0][r][j];
-            for (int w = 1; w < NT / kWave; ++w) z[j] += part[w][r][j];
+#pragma unroll
+        for (int j = 0; j < MK; ++j) {
+            float zz = part[0][r * MK + j];
+#pragma unroll
+            for (int w = 1; w < NWV; ++w) zz += part[w][r * MK + j];
+            z[j] = j < ks ? zz : -INFINITY;
             m = fmaxf(m, z[j]);
         }
         float ex[MK], den = 0.f;
-        for (int j = 0; j < ks; ++j) {
-            ex[j] = expf(z[j] - m);
+#pragma unroll
+        for (int j = 0; j < MK; ++j) {
+            ex[j] = j < ks ? expf(z[j] - m) : 0.f;
             den += ex[j];
         }
-        for (int j = 0; j < ks; ++j) wts[r][j] = ex[j] / den;
-    }
-    __syncthreads();
-    for (int e = tid; e < rows * gs; e += NT) {  // causal taps, zero before the block
-        const int r = e / gs, c = g * gs + e % gs, t = r % B;
+        const float inv = 1.f / den;
         float v = 0.f;
-        for (int j = 0; j < ks; ++j)
-            if (t - j >= 0) v += wts[r][j] * bf16_to_f32(h[(size_t)(r - j) * D + c]);
+#pragma unroll
+        for (int j = 0; j < MK; ++j)
+            if (j < ks && t - j >= 0) v += (ex[j] * inv) * hv[j];
         y[(size_t)r * D + c] = f32_to_bf16(v);
         if (y_f32) y_f32[(size_t)r * D + c] = v;
+    };
+    if (tid < napply) tap(r0, c0, t0, hp);
+    for (int e = tid + NT; e < napply; e += NT) {
+        const int r = e / gs, c = g * gs + e % gs, t = r % B;
+        float hv[MK];
+#pragma unroll
+        for (int j = 0; j < MK; ++j) hv[j] = bf16_to_f32(h[(size_t)max(r - j, 0) * D + c]);
+        tap(r, c, t, hv);
     }
 }
 
@@ -329,13 +428,20 @@ hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y,
     }
     if (d.bf16 && d.rows() <= kConvRowsMax) {
         const dim3 grid(d.groups(), layers);
-        if (d.rows() <= 8 && d.ks <= 2)
-            conv_rows_kernel<8, 2, 256><<<grid, 256, 0, s>>>((const uint16_t*)h, (const uint16_t*)wg_cm,
-                                                            (uint16_t*)y, y_f32, d.rows(), d.B, d.D, d.gs, d.ks, C);
-        else
-            conv_rows_kernel<kConvRowsMax, 4, 256><<<grid, 256, 0, s>>>((const uint16_t*)h,
-                                                                       (const uint16_t*)wg_cm, (uint16_t*)y, y_f32,
-                                                                       d.rows(), d.B, d.D, d.gs, d.ks, C);
+        const auto* hb = (const uint16_t*)h;
+        const auto* wb = (const uint16_t*)wg_cm;
+        auto* yb = (uint16_t*)y;
+        if (d.rows() <= 8 && d.ks <= 2) {
+            if (d.D / 8 > 320)
+                conv_rows_kernel<8, 2, 320, 2><<<grid, 320, 0, s>>>(hb, wb, yb, y_f32, d.rows(), d.B, d.D, d.gs, d.ks,
+                                                                    C);
+            else
+                conv_rows_kernel<8, 2, 320, 1><<<grid, 320, 0, s>>>(hb, wb, yb, y_f32, d.rows(), d.B, d.D, d.gs, d.ks,
+                                                                    C);
+        } else {
+            conv_rows_kernel<kConvRowsMax, 4, 256, 1><<<grid, 256, 0, s>>>(hb, wb, yb, y_f32, d.rows(), d.B, d.D, d.gs,
+                                                                          d.ks, C);
+        }
         return hipGetLastError();
     }
     if (d.bf16) {
