@@ -191,27 +191,44 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
         return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)p));
     };
 
-    // The first weight loads do not depend on the hidden rows: issue them
-    // before staging those.
-    bf16x8 a[U];
-    const uint16_t* cur = tile_ptr(0);
-    if (total > 0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) a[u] = ldw(cur + 64 * u);
-    }
-
     // Hidden rows -> LDS.  16-B unit (s, q, j): row j & 7, channels
     // 64s + 32(j >> 3) + 8q .. +7, so the B operand of k-step s is one
-    // contiguous 1 KB read by the 64 lanes.
-    {
-        uint4* ys = (uint4*)smem;
-        for (int u = threadIdx.x; u < S * 64; u += NW * kWave) {
-            const int j = u & 15, qq = (u >> 4) & 3, s = u >> 6, row = j & 7;
-            uint4 v = {0u, 0u, 0u, 0u};
-            if (row < rows) v = *(const uint4*)(y + (size_t)(row_base + row) * D + 64 * s + 32 * (j >> 3) + 8 * qq);
-            ys[u] = v;
-        }
+    // contiguous 1 KB read by the 64 lanes.  The hidden rows' loads go out
+    // first, all together (a row past `rows` reads row 0 and is stored as
+    // zeros), then the first weight loads, which do not depend on them.
+    // Loads complete in order, so the LDS stores wait on the hidden rows
+    // only and the weight loads stay in flight meanwhile.  (Staged one unit
+    // at a time, every store waited on all loads before it: ten L2 round
+    // trips per workgroup with its weight stream idle.)
+    constexpr int YB = 16;  // hidden-row units per thread in the first batch
+    uint4* ys = (uint4*)smem;
+    const int nyu = S * 64;
+    auto yaddr = [&](int u) -> const uint4* {
+        const int j = u & 15, qq = (u >> 4) & 3, s = u >> 6, row = j & 7;
+        return (const uint4*)(y + (size_t)(row_base + (row < rows ? row : 0)) * D + 64 * s + 32 * (j >> 3) + 8 * qq);
+    };
+    uint4 yv[YB];
+#pragma unroll
+    for (int i = 0; i < YB; ++i) yv[i] = *yaddr(min((int)threadIdx.x + i * NW * kWave, nyu - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    // (Unconditional: with no tile for this wave the address is still a
+    // weight row, clamped, and the data goes unused.)
+    bf16x8 a[U];
+    const uint16_t* cur = tile_ptr(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = ldw(cur + 64 * u);
+    __builtin_amdgcn_sched_barrier(0);
+    // No branch below either (a unit past the end stores the last unit's
+    // data again), so that the wait counts stay exact and no store waits
+    // on the weight loads.
+#pragma unroll
+    for (int i = 0; i < YB; ++i) {
+        const int u = min((int)threadIdx.x + i * NW * kWave, nyu - 1);
+        const uint32_t keep = ((u & 7) < rows) ? 0xFFFFFFFFu : 0u;
+        ys[u] = uint4{yv[i].x & keep, yv[i].y & keep, yv[i].z & keep, yv[i].w & keep};
     }
+    for (int u = threadIdx.x + YB * NW * kWave; u < nyu; u += NW * kWave)  // past the first batch
+        ys[u] = ((u & 7) < rows) ? *yaddr(u) : uint4{0u, 0u, 0u, 0u};
     __syncthreads();
     const uint4* ysb = (const uint4*)smem + q * 16 + i16;
 
