@@ -68,6 +68,13 @@ CONV_SHAPES = [
     S(batch=3, block=16, hidden=64, group=64, ksize=2),
     S(batch=2, block=5, hidden=96, ksize=1, dtype="f32"),
     S(batch=2, block=8, hidden=8192),  # the largest bf16 hidden size
+    # one-launch conv at up to 8 rows: two load passes (D 8192), more causal
+    # taps than threads (groups of 64), one tap with the fp32 output (the
+    # second tap slot weighted 0), a 3-row block
+    S(batch=1, block=8, hidden=8192),
+    S(batch=1, block=8, hidden=512, group=64),
+    S(batch=1, block=6, hidden=3072, ksize=1),
+    S(batch=1, block=3, hidden=2048, group=32),
 ]
 
 
