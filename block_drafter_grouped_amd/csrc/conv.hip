@@ -118,7 +118,12 @@ __global__ __launch_bounds__(kGenWaves * kWave) void conv_gen_kernel(const uint1
 
 // Sums the split partials of a 16-column x 16-row tile of z in split order,
 // applies the softmax over each group's taps, then the causal taps to the
-// 16/ks groups the columns cover.
+// 16/ks groups the columns cover.  With gs % 8 == 0 a thread computes 8
+// consecutive channels of one row from 16-B loads of the hidden rows, and
+// the loads of its first 8 channels go out before the partial sums, which
+// they do not depend on: the tile's loads then take one round instead of a
+// round per output.  MK: compile-time bound of the taps.
+template <int MK>
 __global__ __launch_bounds__(256) void conv_apply_kernel(const uint16_t* __restrict__ h,
                                                          const float* __restrict__ zpart, uint16_t* __restrict__ y,
                                                          float* __restrict__ y_f32, int rows, int B, int D, int gs,
@@ -134,6 +139,21 @@ __global__ __launch_bounds__(256) void conv_apply_kernel(const uint16_t* __restr
         y += l * rows * D;
         if (y_f32) y_f32 += l * rows * D;
     }
+    const int ncol = min(16, C - col0);  // a multiple of ks
+    const int ng = ncol / ks;
+    const int c0 = (col0 / ks) * gs;
+    const int nch = ng * gs;
+    const bool vec = gs % 8 == 0;
+    const int nvec = vec ? 16 * (nch / 8) : 0;  // 8-channel outputs of the tile
+    // Hidden rows r, r - 1, ... at this thread's first 8 channels (addresses
+    // clamped; rows before the block or past the end are not used).
+    auto hvec = [&](int e, uint4 (&hv)[MK]) {
+        const int rr = e / (nch / 8), row = min(row0 + rr, rows - 1), c = c0 + 8 * (e % (nch / 8));
+#pragma unroll
+        for (int j = 0; j < MK; ++j) hv[j] = *(const uint4*)(h + (size_t)max(row - j, 0) * D + c);
+    };
+    uint4 hv0[MK];
+    if (vec) hvec(min(t0, nvec - 1), hv0);
     {
         const int rr = t0 / 16, cc = t0 % 16, row = row0 + rr, col = col0 + cc;
         float z = 0.f;
@@ -142,8 +162,6 @@ __global__ __launch_bounds__(256) void conv_apply_kernel(const uint16_t* __restr
         zt[rr][cc] = z;
     }
     __syncthreads();
-    const int ncol = min(16, C - col0);  // a multiple of ks
-    const int ng = ncol / ks;
     for (int e = t0; e < 16 * ng; e += blockDim.x) {
         const int rr = e / ng, gl = e % ng;
         float m = -INFINITY;
@@ -156,8 +174,44 @@ __global__ __launch_bounds__(256) void conv_apply_kernel(const uint16_t* __restr
         for (int j = 0; j < ks; ++j) wt[rr][gl * ks + j] = ex[j] / den;
     }
     __syncthreads();
-    const int c0 = (col0 / ks) * gs;
-    const int nch = ng * gs;
+    if (vec) {
+        for (int e = t0; e < nvec; e += blockDim.x) {
+            uint4 hv[MK];
+            if (e == t0) {
+#pragma unroll
+                for (int j = 0; j < MK; ++j) hv[j] = hv0[j];
+            } else {
+                hvec(e, hv);
+            }
+            const int rr = e / (nch / 8), row = row0 + rr, cl = 8 * (e % (nch / 8)), gl = cl / gs;
+            if (row >= rows) continue;
+            const int t = row % B;
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < MK; ++j) {
+                if (j < ks && t - j >= 0) {
+                    const float wj = wt[rr][gl * ks + j];
+                    const uint32_t q[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[2 * i] += wj * __uint_as_float(q[i] << 16);
+                        v[2 * i + 1] += wj * __uint_as_float(q[i] & 0xFFFF0000u);
+                    }
+                }
+            }
+            const size_t o = (size_t)row * D + c0 + cl;
+            uint32_t packed[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                packed[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+            *(uint4*)(y + o) = uint4{packed[0], packed[1], packed[2], packed[3]};
+            if (y_f32) {
+                *(f32x4*)(y_f32 + o) = f32x4{v[0], v[1], v[2], v[3]};
+                *(f32x4*)(y_f32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            }
+        }
+        return;
+    }
     for (int e = t0; e < 16 * nch; e += blockDim.x) {
         const int rr = e / nch, cc = e % nch;
         const int row = row0 + rr;
@@ -465,8 +519,12 @@ hipError_t launch_conv(const Dims& d, const void* h, const void* wg_cm, void* y,
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         dim3 grid2((C + 15) / 16, (d.rows() + 15) / 16, layers);
-        conv_apply_kernel<<<grid2, 256, 0, s>>>((const uint16_t*)h, zpart, (uint16_t*)y, y_f32, d.rows(), d.B, d.D,
-                                                d.gs, d.ks, C);
+        if (d.ks <= 2)
+            conv_apply_kernel<2><<<grid2, 256, 0, s>>>((const uint16_t*)h, zpart, (uint16_t*)y, y_f32, d.rows(), d.B,
+                                                       d.D, d.gs, d.ks, C);
+        else
+            conv_apply_kernel<4><<<grid2, 256, 0, s>>>((const uint16_t*)h, zpart, (uint16_t*)y, y_f32, d.rows(), d.B,
+                                                       d.D, d.gs, d.ks, C);
     } else {
         conv_f32_kernel<<<dim3(d.rows(), layers), 256, 2 * (size_t)C * sizeof(float), s>>>(
             (const float*)h, (const float*)wg_cm, (float*)y, y_f32, d.rows(), d.B, d.D, d.gs, d.ks, C);

@@ -75,6 +75,10 @@ CONV_SHAPES = [
     S(batch=1, block=8, hidden=512, group=64),
     S(batch=1, block=6, hidden=3072, ksize=1),
     S(batch=1, block=3, hidden=2048, group=32),
+    # split-D conv (more than 16 rows): groups of 4 channels (the per-channel
+    # apply), four taps
+    S(batch=3, block=8, hidden=128, group=4),
+    S(batch=5, block=8, hidden=256, ksize=4),
 ]
 
 
