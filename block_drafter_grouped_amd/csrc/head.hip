@@ -33,6 +33,38 @@ namespace {
 
 constexpr size_t kMinHeadLds = 82 * 1024;  // > 80 KB: one workgroup per CU
 
+// Top K of at most 16 sorted lists (descending, distinct keys, empty entries
+// 0) held in LDS, list l read by lane l of row 0 (lanes 0-15); out[i *
+// out_stride] receives the i-th largest key, written by lane 0.  As
+// wave_tournament, but a round's maximum over the 16 heads takes four DPP
+// steps inside row 0 (no lane readback, no scalar compare), and every lane
+// has its next key loaded a round ahead, so the LDS read is off the chain
+// of a round.  (With the 64-lane maximum and a dependent LDS read per
+// round, the merge of the 16 lists of a row took about 5 us at the end of
+// the streaming head.)
+__device__ __forceinline__ void row_tournament16(const uint64_t* lists, int nsrc, int stride, int len, int K,
+                                                 uint64_t* out, int out_stride) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool src = lane < nsrc && lane < 16;
+    const uint64_t* my = lists + (size_t)(src ? lane : 0) * stride;
+    int head = 0;
+    uint64_t key = (src && len > 0) ? my[0] : 0ull;
+    uint64_t nxt = (src && len > 1) ? my[1] : 0ull;
+    for (int round = 0; round < K; ++round) {
+        uint64_t mx = key;
+        mx = umax64(mx, dpp_u64<kDppQuadXor1>(mx));
+        mx = umax64(mx, dpp_u64<kDppQuadXor2>(mx));
+        mx = umax64(mx, dpp_u64<kDppHalfMirror>(mx));
+        mx = umax64(mx, dpp_u64<kDppMirror>(mx));  // every lane of row 0: the largest head
+        if (lane == 0) out[(size_t)round * out_stride] = mx;
+        if (src && mx != 0ull && key == mx) {
+            ++head;
+            key = nxt;
+            nxt = head + 1 < len ? my[head + 1] : 0ull;
+        }
+    }
+}
+
 template <int NW, int U, int KL>
 __global__ __launch_bounds__(NW * kWave) void head_bf16_kernel(
     const uint16_t* __restrict__ y, int rows_total, int D, const uint16_t* __restrict__ W, int V, int nch, int K,
@@ -168,6 +200,7 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int KL = 16;
     constexpr int NSRC = NW * 2;  // two lanes per row per wave carry results
+    static_assert(NSRC <= 16, "the lists of a row fit in 16 lanes");
     const int c = blockIdx.x;
     const int row_base = blockIdx.y * kRowsPass;
     const int rows = min(kRowsPass, rows_total - row_base);
@@ -297,7 +330,7 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
     }
     __syncthreads();
     for (int jr = wave; jr < rows; jr += NW) {
-        wave_tournament(L + (size_t)jr * NSRC * K, NSRC, K, K, K, part_keys + (size_t)(row_base + jr) * K * nch + c,
+        row_tournament16(L + (size_t)jr * NSRC * K, NSRC, K, K, K, part_keys + (size_t)(row_base + jr) * K * nch + c,
                         nch);
         MaxSum x{-INFINITY, 0.f};
         if (lane < NSRC) {
