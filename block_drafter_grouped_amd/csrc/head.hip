@@ -34,19 +34,17 @@ namespace {
 constexpr size_t kMinHeadLds = 82 * 1024;  // > 80 KB: one workgroup per CU
 
 // Top K of at most 16 sorted lists (descending, distinct keys, empty entries
-// 0) held in LDS, list l read by lane l of row 0 (lanes 0-15); out[i *
-// out_stride] receives the i-th largest key, written by lane 0.  As
-// wave_tournament, but a round's maximum over the 16 heads takes four DPP
-// steps inside row 0 (no lane readback, no scalar compare), and every lane
-// has its next key loaded a round ahead, so the LDS read is off the chain
-// of a round.  (With the 64-lane maximum and a dependent LDS read per
-// round, the merge of the 16 lists of a row took about 5 us at the end of
-// the streaming head.)
-__device__ __forceinline__ void row_tournament16(const uint64_t* lists, int nsrc, int stride, int len, int K,
-                                                 uint64_t* out, int out_stride) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const bool src = lane < nsrc && lane < 16;
-    const uint64_t* my = lists + (size_t)(src ? lane : 0) * stride;
+// 0) per DPP row: the 16 lanes of a row (lanes 16 r .. 16 r + 15) each read
+// one list (`my`, when `src`), and a row's writer lane receives the i-th
+// largest key of the row's lists in out[i * out_stride].  One wave thus
+// merges the lists of four rows at once.  As wave_tournament, but a round's
+// maximum takes four DPP steps inside each row (no lane readback), and every
+// lane has its next key loaded a round ahead, so the LDS read is off the
+// chain of a round.  (With a 64-lane maximum, a dependent LDS read per round
+// and one row per wave, two waves sharing each SIMD, the merge of the lists
+// took about 5 us at the end of the streaming head.)
+__device__ __forceinline__ void row_tournament16(const uint64_t* my, bool src, int len, int K, uint64_t* out,
+                                                 int out_stride, bool writer) {
     int head = 0;
     uint64_t key = (src && len > 0) ? my[0] : 0ull;
     uint64_t nxt = (src && len > 1) ? my[1] : 0ull;
@@ -55,8 +53,8 @@ __device__ __forceinline__ void row_tournament16(const uint64_t* lists, int nsrc
         mx = umax64(mx, dpp_u64<kDppQuadXor1>(mx));
         mx = umax64(mx, dpp_u64<kDppQuadXor2>(mx));
         mx = umax64(mx, dpp_u64<kDppHalfMirror>(mx));
-        mx = umax64(mx, dpp_u64<kDppMirror>(mx));  // every lane of row 0: the largest head
-        if (lane == 0) out[(size_t)round * out_stride] = mx;
+        mx = umax64(mx, dpp_u64<kDppMirror>(mx));  // every lane of a row: the row's largest head
+        if (writer) out[(size_t)round * out_stride] = mx;
         if (src && mx != 0ull && key == mx) {
             ++head;
             key = nxt;
@@ -200,7 +198,7 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int KL = 16;
     constexpr int NSRC = NW * 2;  // two lanes per row per wave carry results
-    static_assert(NSRC <= 16, "the lists of a row fit in 16 lanes");
+    static_assert(NSRC <= 16 && kRowsPass <= 8, "the lists of a row fit in one DPP row; two waves merge");
     const int c = blockIdx.x;
     const int row_base = blockIdx.y * kRowsPass;
     const int rows = min(kRowsPass, rows_total - row_base);
@@ -329,16 +327,23 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
         M[i16 * NSRC + src] = make_float2(ms.m, ms.s);
     }
     __syncthreads();
-    for (int jr = wave; jr < rows; jr += NW) {
-        row_tournament16(L + (size_t)jr * NSRC * K, NSRC, K, K, K, part_keys + (size_t)(row_base + jr) * K * nch + c,
-                        nch);
+    // Waves 0 and 1 merge: DPP row r of wave w takes row 4 w + r, one list
+    // per lane.  (Each alone on its SIMD: the rounds run at full issue rate.)
+    if (wave < (rows + 3) / 4) {
+        const int l = lane & 15, jr = 4 * wave + (lane >> 4);
+        const bool live = jr < rows && l < NSRC, writer = l == 0 && jr < rows;
+        row_tournament16(L + ((size_t)(live ? jr : 0) * NSRC + (live ? l : 0)) * K, live, K, K,
+                         part_keys + (size_t)(row_base + (jr < rows ? jr : 0)) * K * nch + c, nch, writer);
         MaxSum x{-INFINITY, 0.f};
-        if (lane < NSRC) {
-            const float2 p = M[jr * NSRC + lane];
+        if (live) {
+            const float2 p = M[jr * NSRC + l];
             x = MaxSum{p.x, p.y};
         }
-        x = wave_ms_reduce(x);
-        if (lane == 0) part_ms[(size_t)(row_base + jr) * nch + c] = make_float2(x.m, x.s);
+        x = ms_dpp_step<kDppQuadXor1>(x);  // inside each row, in a fixed order
+        x = ms_dpp_step<kDppQuadXor2>(x);
+        x = ms_dpp_step<kDppHalfMirror>(x);
+        x = ms_dpp_step<kDppMirror>(x);
+        if (writer) part_ms[(size_t)(row_base + jr) * nch + c] = make_float2(x.m, x.s);
     }
 }
 
