@@ -281,11 +281,22 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
         }
         const uint16_t* nxt = (g + 1 < total) ? (ngi == 0 ? tile_ptr(nti) : cur + 64 * U) : cur;
         const int s0 = gi * U;
+        if (g + 1 < total) {  // wave-uniform
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bf16x8 b = *(const bf16x8*)(ysb + (size_t)(s0 + u) * 64);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b, acc, 0, 0, 0);
-            a[u] = ldw(nxt + 64 * u);
+            for (int u = 0; u < U; ++u) {
+                const bf16x8 b = *(const bf16x8*)(ysb + (size_t)(s0 + u) * 64);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b, acc, 0, 0, 0);
+                a[u] = ldw(nxt + 64 * u);
+            }
+        } else {
+            // The last group issues no loads: nothing follows, and the
+            // barrier after the loop would wait for them (an 8 KB reload per
+            // wave, with its latency, at the end of the slowest wave).
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bf16x8 b = *(const bf16x8*)(ysb + (size_t)(s0 + u) * 64);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b, acc, 0, 0, 0);
+            }
         }
         if (ngi == 0) {
             float v4[4];
