@@ -12,8 +12,10 @@
 //
 // bf16 streaming head (up to 8 rows): the work is a stream of the [V, D]
 // weight (2.5 GB at D 5120, V 248 320) against a tiny [rows, D] operand, so
-// it is bound by HBM.  One persistent workgroup per CU owns a contiguous
-// range of vocabulary tiles; the hidden rows sit in LDS for the whole kernel,
+// it is bound by HBM.  One persistent workgroup per CU owns every nch-th
+// vocabulary tile (tiles c, c + nch, ...: at any time the workgroups stream
+// neighbouring tiles, which measured 2 % faster at the page shape than
+// contiguous ranges per workgroup); the hidden rows sit in LDS for the whole kernel,
 // pre-swizzled into MFMA B-operand order, and every wave streams its tiles
 // with v_mfma_f32_16x16x32_bf16 while U k-steps of weight loads are in
 // flight.  The MFMA's 16 output columns hold the (<= 8) rows, so part of each
@@ -90,16 +92,17 @@ __global__ __launch_bounds__(NW * kWave) void head_bf16_kernel(
     }
     __syncthreads();
 
+    // Chunk c owns tiles c, c + nch, ... (as in head_pair_kernel, below).
     const int64_t T = ((int64_t)V + 15) / 16;
-    const int t_beg = (int)(T * c / nch), t_end = (int)(T * (c + 1) / nch);
-    const int my_n = (t_end - t_beg - wave + NW - 1) / NW;
+    const int cnt_c = (int)((T - c + nch - 1) / nch);
+    const int my_n = max(0, (cnt_c - wave + NW - 1) / NW);
     const int i16 = lane & 15, q = lane >> 4, jrow = lane & 15;
     const int GPT = S / U;  // k-step groups per tile
     const int total = my_n * GPT;
     const uint4* ysb = (const uint4*)smem + q * kRowsPass + (lane & 7);
 
     auto tile_ptr = [&](int i) -> const uint16_t* {
-        const int tt = t_beg + wave + i * NW;
+        const int tt = c + nch * (wave + i * NW);
         const int v = min(tt * 16 + i16, V - 1);
         return W + (size_t)v * D + 8 * q;
     };
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(NW * kWave) void head_bf16_kernel(
         }
         if (ngi == 0) {
             // Tile done: lane holds logit[v0 + 4q + r][row jrow] in acc[r].
-            const int v0 = (t_beg + wave + ti * NW) * 16 + 4 * q;
+            const int v0 = (c + nch * (wave + ti * NW)) * 16 + 4 * q;
             if (jrow < rows) {
                 float mnew = ms.m;
 #pragma unroll
@@ -206,15 +209,18 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
     const int S = D / 64;
     const int i16 = lane & 15, q = lane >> 4;
 
+    // Chunk c owns tiles c, c + nch, c + 2 nch, ... (wave w its w-th, (w +
+    // NW)-th, ... of them), so that at any time the workgroups stream
+    // neighbouring tiles.
     const int64_t T = ((int64_t)V + 7) / 8;
-    const int t_beg = (int)(T * c / nch), t_end = (int)(T * (c + 1) / nch);
-    const int my_n = (t_end - t_beg - wave + NW - 1) / NW;
+    const int cnt_c = (int)((T - c + nch - 1) / nch);
+    const int my_n = max(0, (cnt_c - wave + NW - 1) / NW);
     const int GPT = S / U;
     const int total = my_n * GPT;
     const int a_off = 32 * (i16 >> 3) + 8 * q;
 
     auto tile_ptr = [&](int i) -> const uint16_t* {
-        const int tt = t_beg + wave + i * NW;
+        const int tt = c + nch * (wave + i * NW);
         const int v = min(tt * 8 + (i16 & 7), V - 1);
         return W + (size_t)v * D + a_off;
     };
@@ -302,7 +308,7 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
             float v4[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) v4[r] = acc[r] + __shfl(acc[r], (lane + 40) & (kWave - 1), kWave);
-            const int v0 = (t_beg + wave + ti * NW) * 8 + 4 * q;
+            const int v0 = (c + nch * (wave + ti * NW)) * 8 + 4 * q;
             if (owner) {
                 float mnew = ms.m;
 #pragma unroll
