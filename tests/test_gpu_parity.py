@@ -834,6 +834,77 @@ def test_draft_block_equals_separate_calls(case):
         assert np.array_equal(from_dev(ids), np.tile(np.arange(s.top_k, dtype=np.int32), (s.rows, 1)))
 
 
+SMALL_BLOCK_CASES = [
+    # (shape, options, anchor of block 1 replaced by an invalid id)
+    (S(batch=1, block=8, hidden=256, vocab=9001, top_k=16, rank=64), {}, False),
+    (S(batch=1, block=2, hidden=128, vocab=5000, top_k=16, rank=32), {}, False),
+    (S(batch=2, block=4, hidden=256, vocab=7001, top_k=8, rank=64), dict(walk="greedy"), False),
+    (S(batch=4, block=2, hidden=128, vocab=3000, top_k=5, rank=32), dict(walk="sample", temperature=0.7), False),
+    (S(batch=1, block=7, hidden=192, vocab=6000, top_k=1, rank=32), {}, False),
+    (S(batch=1, block=8, hidden=160, vocab=6000, top_k=12, rank=64), dict(gate=True), False),
+    (S(batch=2, block=3, hidden=256, vocab=4099, top_k=16, rank=96), dict(gate=True, walk="sample", temperature=1.3),
+     False),
+    (S(batch=2, block=4, hidden=128, vocab=5000, top_k=16, rank=64), {}, True),
+    (S(batch=1, block=8, hidden=1024, vocab=50000, top_k=16, rank=256, ksize=1), {}, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_BLOCK_CASES, ids=lambda c: f"{c[0]}-{sorted(c[1])}-bad{int(c[2])}")
+def test_draft_block_few_rows_equals_separate_calls(case):
+    """Up to 8 rows (the streaming head), dfs_draft_block gives the same bits
+    as dfs_conv, dfs_head_topk and dfs_select: candidates, log-probabilities,
+    path and score, for every walk rule, with and without a gate, one to four
+    blocks, an invalid anchor (that block only is marked), D not a multiple
+    of 64 (the other streaming head), one tap.  The workspace starts as
+    all-ones bytes, and a second call on it gives the same bits: nothing
+    depends on what an earlier call left there."""
+    s, opts, bad = case
+    inp = wl.make_inputs_for(s, 41)
+    dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
+    dev["wg_cm"] = to_dev(wg_channel_major(inp["wg"]))
+    if bad:
+        a = inp["anchor"].copy()
+        a[1] = -1
+        dev["anchor"] = to_dev(a)
+    opts = dict(opts)
+    if opts.pop("gate", False):
+        opts["gate"] = to_dev(gate_for(s, 42))
+    if opts.get("walk") == "sample":
+        opts["uniforms"] = to_dev(np.random.default_rng(43).random((s.batch, s.block)).astype(np.float32))
+    cfg = dfs.Config.of(s)
+    ws = torch.full((dfs.workspace_size(cfg),), 255, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        path = empty((s.batch, s.block), torch.int32)
+        score = empty((s.batch,), torch.float32)
+        ids = empty((s.rows, s.top_k), torch.int32)
+        lp = empty((s.rows, s.top_k), torch.float32)
+        dfs.draft_block(cfg, dev["h"], dev["anchor"], dev["wg_cm"], dev["W"], dev["P"], dev["Q"], path, score, ws,
+                        cand_ids=ids, cand_logp=lp, **opts)
+        torch.cuda.synchronize()
+        outs.append([from_dev(x) for x in (path, score, ids, lp)])
+    y = empty((s.rows, s.hidden), torch.int16)
+    ids2 = empty((s.rows, s.top_k), torch.int32)
+    lp2 = empty((s.rows, s.top_k), torch.float32)
+    lse2 = empty((s.rows,), torch.float32)
+    path2 = empty((s.batch, s.block), torch.int32)
+    score2 = empty((s.batch,), torch.float32)
+    if s.ksize == 1:
+        y = dev["h"]
+    else:
+        dfs.conv(cfg, dev["h"], dev["wg_cm"], y, wsbuf(cfg))
+    dfs.head_topk(cfg, y, dev["W"], ids2, lp2, lse2, wsbuf(cfg))
+    dfs.select(cfg, dev["anchor"], ids2, lp2, dev["P"], dev["Q"], path2, score2, wsbuf(cfg), **opts)
+    torch.cuda.synchronize()
+    ref = [from_dev(x) for x in (path2, score2, ids2, lp2)]
+    for out in outs:
+        for x, r in zip(out, ref):
+            assert np.array_equal(x, r, equal_nan=True)
+    if bad:
+        assert np.all(ref[0][1] == -1) and np.isnan(ref[1][1])
+        assert np.all(ref[0][0] >= 0) and not np.isnan(ref[1][0])
+
+
 def test_draft_block_deterministic_and_stream():
     s = wl.shape_of(2)
     inp, dev = cfg_inputs(2)
