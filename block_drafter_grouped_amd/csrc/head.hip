@@ -35,35 +35,7 @@ namespace {
 
 constexpr size_t kMinHeadLds = 82 * 1024;  // > 80 KB: one workgroup per CU
 
-// Top K of at most 16 sorted lists (descending, distinct keys, empty entries
-// 0) per DPP row: the 16 lanes of a row (lanes 16 r .. 16 r + 15) each read
-// one list (`my`, when `src`), and a row's writer lane receives the i-th
-// largest key of the row's lists in out[i * out_stride].  One wave thus
-// merges the lists of four rows at once.  As wave_tournament, but a round's
-// maximum takes four DPP steps inside each row (no lane readback), and every
-// lane has its next key loaded a round ahead, so the LDS read is off the
-// chain of a round.  (With a 64-lane maximum, a dependent LDS read per round
-// and one row per wave, two waves sharing each SIMD, the merge of the lists
-// took about 5 us at the end of the streaming head.)
-__device__ __forceinline__ void row_tournament16(const uint64_t* my, bool src, int len, int K, uint64_t* out,
-                                                 int out_stride, bool writer) {
-    int head = 0;
-    uint64_t key = (src && len > 0) ? my[0] : 0ull;
-    uint64_t nxt = (src && len > 1) ? my[1] : 0ull;
-    for (int round = 0; round < K; ++round) {
-        uint64_t mx = key;
-        mx = umax64(mx, dpp_u64<kDppQuadXor1>(mx));
-        mx = umax64(mx, dpp_u64<kDppQuadXor2>(mx));
-        mx = umax64(mx, dpp_u64<kDppHalfMirror>(mx));
-        mx = umax64(mx, dpp_u64<kDppMirror>(mx));  // every lane of a row: the row's largest head
-        if (writer) out[(size_t)round * out_stride] = mx;
-        if (src && mx != 0ull && key == mx) {
-            ++head;
-            key = nxt;
-            nxt = head + 1 < len ? my[head + 1] : 0ull;
-        }
-    }
-}
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 template <int NW, int U, int KL>
 __global__ __launch_bounds__(NW * kWave) void head_bf16_kernel(
@@ -266,6 +238,16 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
     }
     for (int u = threadIdx.x + YB * NW * kWave; u < nyu; u += NW * kWave)  // past the first batch
         ys[u] = ((u & 7) < rows) ? *yaddr(u) : uint4{0u, 0u, 0u, 0u};
+    // The tail's lists live past the hidden rows, which the other waves still
+    // read while a wave that is done stores its own.
+    uint64_t* run = (uint64_t*)(smem + (size_t)nyu * 16);  // [kRowsPass][KL]
+    float2* MW = (float2*)(run + kRowsPass * KL);            // [NW][kRowsPass]
+    int* arrived = (int*)(MW + NW * kRowsPass);
+    int* merged = arrived + 1;
+    if (threadIdx.x == 0) {
+        *arrived = 0;
+        *merged = 0;
+    }
     __syncthreads();
     const uint4* ysb = (const uint4*)smem + q * 16 + i16;
 
@@ -332,36 +314,82 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
         ti = nti;
         gi = ngi;
     }
-    __syncthreads();  // LDS switches from hidden rows to the merge lists
-
-    uint64_t* L = (uint64_t*)smem;                                     // [kRowsPass][NSRC][K]
-    float2* M = (float2*)(smem + (size_t)kRowsPass * NSRC * K * 8);  // [kRowsPass][NSRC]
-    if (owner) {
-        const int src = wave * 2 + q;
+    // Tail, per wave as soon as its own tiles are done.  Lane i16 < 8 (q =
+    // 0) takes the list and (max, sum of exp) of lane i16 + 16 (q = 1, the
+    // same row, the other half of the tile's vocabulary) through
+    // v_permlane16_swap and merges them.  The waves then fold their lists
+    // into running lists in LDS in the order they arrive (lane r: row r),
+    // each waiting for the wave before it, so the last wave merges once.
+    // The union's top KL keys do not depend on that order.  The (max, sum of
+    // exp) pairs go to LDS per wave, and the last wave folds them in a fixed
+    // tree (lane 8 r + w: row r, wave w; wave w with w ^ 1, w ^ 2, then the
+    // mirrored half), which pairs the same operands as a butterfly over the
+    // 2 NW lists in (wave, half) order.  (After a barrier for all waves, a
+    // tournament over the 16 lists of every row took 4.4 us from the last
+    // wave's last tile to the stored partials; a tree over the waves' lists
+    // in the last wave, 4.3 us: one wave64 issues a VALU operation every
+    // four cycles.)
+    {
+        uint64_t oth[KL];
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+            const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)lst[i], (uint32_t)lst[i], false, false);
+            const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(lst[i] >> 32), (uint32_t)(lst[i] >> 32),
+                                                             false, false);
+            oth[i] = ((uint64_t)hi[1] << 32) | lo[1];  // rows 0 and 2 of the wave: lane + 16
+        }
+        merge_top<KL>(lst, oth);
+        const auto pm = __builtin_amdgcn_permlane16_swap(__float_as_uint(ms.m), __float_as_uint(ms.m), false, false);
+        const auto ps = __builtin_amdgcn_permlane16_swap(__float_as_uint(ms.s), __float_as_uint(ms.s), false, false);
+        ms = ms_combine(ms, MaxSum{__uint_as_float(pm[1]), __uint_as_float(ps[1])});
+    }
+    if (lane < kRowsPass) MW[wave * kRowsPass + lane] = make_float2(ms.m, ms.s);
+    int ticket = 0;
+    if (lane == 0) ticket = __hip_atomic_fetch_add(arrived, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    uint64_t* my_run = run + (size_t)(lane & (kRowsPass - 1)) * KL;
+    if (ticket > 0) {
+        // The wave before this one in arrival order has its lists in: it
+        // started before this wave arrived and waits for no later wave.
+        // (The bound only guards against a hang; it is never reached.)
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(merged, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == ticket) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane < kRowsPass) {
+            uint64_t oth[KL];
+#pragma unroll
+            for (int i = 0; i < KL; i += 2) {
+                const u64x2 v = *(const u64x2*)(my_run + i);
+                oth[i] = v[0];
+                oth[i + 1] = v[1];
+            }
+            merge_top<KL>(lst, oth);
+        }
+    }
+    if (ticket < NW - 1) {
+        if (lane < kRowsPass) {
+#pragma unroll
+            for (int i = 0; i < KL; i += 2) *(u64x2*)(my_run + i) = u64x2{lst[i], lst[i + 1]};
+        }
+        if (lane == 0) __hip_atomic_store(merged, ticket + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return;  // wave-uniform
+    }
+    // The last wave: lane r < 8 holds the workgroup's top KL keys of row r.
+    if (lane < rows) {
+        uint64_t* out = part_keys + (size_t)(row_base + lane) * K * nch + c;
 #pragma unroll
         for (int i = 0; i < KL; ++i)
-            if (i < K) L[((size_t)i16 * NSRC + src) * K + i] = lst[i];
-        M[i16 * NSRC + src] = make_float2(ms.m, ms.s);
+            if (i < K) out[(size_t)i * nch] = lst[i];
     }
-    __syncthreads();
-    // Waves 0 and 1 merge: DPP row r of wave w takes row 4 w + r, one list
-    // per lane.  (Each alone on its SIMD: the rounds run at full issue rate.)
-    if (wave < (rows + 3) / 4) {
-        const int l = lane & 15, jr = 4 * wave + (lane >> 4);
-        const bool live = jr < rows && l < NSRC, writer = l == 0 && jr < rows;
-        row_tournament16(L + ((size_t)(live ? jr : 0) * NSRC + (live ? l : 0)) * K, live, K, K,
-                         part_keys + (size_t)(row_base + (jr < rows ? jr : 0)) * K * nch + c, nch, writer);
-        MaxSum x{-INFINITY, 0.f};
-        if (live) {
-            const float2 p = M[jr * NSRC + l];
-            x = MaxSum{p.x, p.y};
-        }
-        x = ms_dpp_step<kDppQuadXor1>(x);  // inside each row, in a fixed order
-        x = ms_dpp_step<kDppQuadXor2>(x);
-        x = ms_dpp_step<kDppHalfMirror>(x);
-        x = ms_dpp_step<kDppMirror>(x);
-        if (writer) part_ms[(size_t)(row_base + jr) * nch + c] = make_float2(x.m, x.s);
-    }
+    static_assert(NW == 8 && kRowsPass == 8, "lane 8 r + w: row r, wave w");
+    const int r = lane >> 3, w = lane & 7;
+    const float2 p = MW[w * kRowsPass + r];
+    MaxSum x{p.x, p.y};
+    x = ms_dpp_step<kDppQuadXor1>(x);
+    x = ms_dpp_step<kDppQuadXor2>(x);
+    x = ms_dpp_step<kDppHalfMirror>(x);
+    if (w == 0 && r < rows) part_ms[(size_t)(row_base + r) * nch + c] = make_float2(x.m, x.s);
 }
 
 // Chunk partials -> candidates.  Partial keys are stored element-major,
@@ -651,9 +679,9 @@ template <int NW, int U>
 hipError_t launch_head_pair_t(const Dims& d, int K, const void* y, const void* W, int nch, uint64_t* keys,
                               float2* ms, float* logits, hipStream_t s) {
     const int S = d.D / 64;
-    size_t lds = (size_t)S * 64 * 16;
-    const size_t merge = (size_t)kRowsPass * NW * 2 * K * 8 + (size_t)kRowsPass * NW * 2 * 8;
-    lds = std::max(std::max(lds, merge), kMinHeadLds);
+    // hidden rows, then the tail's running lists, pairs and counters
+    const size_t lds = std::max((size_t)S * 64 * 16 + (size_t)kRowsPass * 16 * 8 + (size_t)NW * kRowsPass * 8 + 16,
+                                kMinHeadLds);
     auto fn = head_pair_kernel<NW, U>;
     static LdsAttr attr;
     hipError_t e = ensure_lds(attr, (const void*)fn, (int)lds);
