@@ -737,6 +737,37 @@ def random_long_configs(n, seed=2028):
     return out
 
 
+def random_large_configs(n, seed=2029):
+    """Seeded configurations at larger sizes: hidden up to 8192 (the bf16
+    limit), vocabularies up to 100 000, blocks up to 64 slots, up to 32
+    blocks, K up to 64, one, two or four taps, both dtypes; rows x V x D is
+    kept under 3e9 so that the oracle finishes in seconds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        hidden = int(rng.choice([96, 320, 640, 1024, 1536, 2048, 2560, 4096, 5120, 8192]))
+        group = int(rng.choice([g for g in (4, 8, 16, 32, 64) if hidden % g == 0]))
+        top_k = int(rng.choice([1, 3, 8, 12, 16, 17, 24, 32, 48, 64]))
+        block = int(rng.choice([2, 4, 8, 9, 16, 24, 32, 48, 64]))
+        batch = int(rng.integers(1, 33)) if rng.random() < 0.6 else 1
+        vocab = int(rng.integers(max(top_k, 16), 100001))
+        ksize = int(rng.choice([1, 2, 2, 4]))
+        dtype = "f32" if rng.random() < 0.2 else "bf16"
+        if batch * block * vocab * hidden > 3e9 or (dtype == "f32" and hidden // group * ksize > 4096):
+            continue
+        out.append(S(batch=batch, block=block, hidden=hidden, vocab=vocab, top_k=top_k,
+                     rank=int(rng.choice([8, 32, 96, 256])), group=group, ksize=ksize, dtype=dtype))
+    return out
+
+
+@pytest.mark.parametrize("s", random_large_configs(16), ids=str)
+def test_draft_block_random_large_configs(s):
+    inp = wl.make_inputs_for(s, 37)
+    dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
+    dev["wg_cm"] = to_dev(wg_channel_major(inp["wg"]))
+    check_block_e2e(s, inp, dev)
+
+
 @pytest.mark.parametrize("s", random_configs(24) + random_long_configs(8), ids=str)
 def test_draft_block_random_configs(s):
     inp = wl.make_inputs_for(s, 23)
