@@ -382,9 +382,9 @@ __global__ __launch_bounds__(NW * kWave) void head_pair_kernel(
         for (int i = 0; i < KL; ++i)
             if (i < K) out[(size_t)i * nch] = lst[i];
     }
-    static_assert(NW <= 8 && kRowsPass == 8, "lane 8 r + w: row r, wave w");
+    static_assert(NW == 8 && kRowsPass == 8, "lane 8 r + w: row r, wave w");
     const int r = lane >> 3, w = lane & 7;
-    const float2 p = w < NW ? MW[w * kRowsPass + r] : make_float2(-INFINITY, 0.f);
+    const float2 p = MW[w * kRowsPass + r];
     MaxSum x{p.x, p.y};
     x = ms_dpp_step<kDppQuadXor1>(x);
     x = ms_dpp_step<kDppQuadXor2>(x);
