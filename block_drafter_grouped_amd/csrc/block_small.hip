@@ -140,9 +140,12 @@ __global__ __launch_bounds__(kSmallThreads) void block_small_kernel(
 
     // 1. conv.  The first 64 channels of this thread's generator row are
     // requested before the hidden rows are staged, so both loads overlap.
+    // The anchor is read now too: the transition scores need it after the
+    // top-K, and then its load would be one more round trip on their path.
     float pre[8][8];
     if (ks != 1 && wave * kWave < taps)  // wave-uniform: only the waves that own generator rows
         load_chunk<T>(wg + (size_t)min(tid, taps - 1) * D, 0, D, pre);
+    const int a = anchor[b];
     const T* hb = h + (size_t)b * B * D;
     for (int i = tid; i < B * D; i += kSmallThreads) hs[i / D][i % D] = elem(hb, i);
     __syncthreads();
@@ -234,7 +237,6 @@ __global__ __launch_bounds__(kSmallThreads) void block_small_kernel(
             }
         }
     }
-    const int a = anchor[b];
     if (a < 0 || a >= V) {  // block-uniform
         write_bad_block(b, B, path, path_score, nullptr);
         return;
