@@ -1,6 +1,7 @@
 """A whole draft block captured in a HIP graph (through torch.cuda.graph) and
-replayed: every replay is compared with the oracle on the same seeded
-inputs, and must reproduce the eager result bit for bit.  The
+replayed: every replay must reproduce the eager result bit for bit, and the
+replays of the default selector are also compared with the oracle on the
+same seeded inputs.  The
 library allocates, frees and synchronises nothing and takes the caller's
 stream, so a caller can capture a step to cut launch overhead on
 launch-bound shapes.  Between replays the test runs its own eager work
@@ -28,11 +29,32 @@ def S(**kw):
 
 @pytest.mark.parametrize("s", [
     S(batch=1, block=8, hidden=512, vocab=20000, top_k=16, rank=256),   # streaming head, fused selector
-    S(batch=6, block=8, hidden=256, vocab=9001, top_k=16, rank=64),     # GEMM head + slice top-K
-    S(batch=2, block=6, hidden=128, vocab=3000, top_k=24, rank=32),     # K > 16: general selector
+    S(batch=6, block=8, hidden=256, vocab=9001, top_k=16, rank=64),     # GEMM head (512-wide tiles), segment merge
+    S(batch=20, block=8, hidden=256, vocab=9001, top_k=16, rank=64),    # GEMM head (256 x 256 tiles), segment merge
+    S(batch=2, block=6, hidden=128, vocab=3000, top_k=24, rank=32),     # K > 16: slice top-K, general selector
     wl.shape_of(0),                                                    # fp32
 ], ids=str)
 def test_draft_block_graph_replay(s):
+    replay_and_check(s, {})
+
+
+@pytest.mark.parametrize("s,walk", [
+    (S(batch=1, block=8, hidden=512, vocab=20000, top_k=16, rank=256), "greedy"),   # fused selector, gated
+    (S(batch=3, block=8, hidden=256, vocab=7001, top_k=16, rank=64), "sample"),     # GEMM head, fused selector
+    (S(batch=2, block=20, hidden=128, vocab=3000, top_k=24, rank=32), "viterbi"),   # general selector, gated
+], ids=str)
+def test_draft_block_graph_replay_with_options(s, walk):
+    """The same with a context gate and each walk rule: every replay gives
+    the eager result bit for bit (the oracle comparison of these options is
+    the parity suite's)."""
+    rng = np.random.default_rng(29)
+    opts = dict(gate=to_dev((0.5 + rng.random((s.rows, s.rank))).astype(np.float32)), walk=walk)
+    if walk == "sample":
+        opts.update(temperature=0.8, uniforms=to_dev(rng.random((s.batch, s.block)).astype(np.float32)))
+    replay_and_check(s, opts)
+
+
+def replay_and_check(s, opts):
     inp = wl.make_inputs_for(s, 23)
     dev = {k: to_dev(v) for k, v in inp.items() if k != "wg"}
     dev["wg_cm"] = to_dev(wg_channel_major(inp["wg"]))
@@ -45,7 +67,7 @@ def test_draft_block_graph_replay(s):
 
     def step():
         dfs.draft_block(cfg, dev["h"], dev["anchor"], dev["wg_cm"], dev["W"], dev["P"], dev["Q"], path, score, ws,
-                        cand_ids=ids, cand_logp=lp)
+                        cand_ids=ids, cand_logp=lp, **opts)
 
     step()
     torch.cuda.synchronize()
@@ -70,6 +92,7 @@ def test_draft_block_graph_replay(s):
         g.replay()
         torch.cuda.synchronize()
         got = [from_dev(t) for t in (path, score, ids, lp)]
-        e2e.check_block_e2e(orc, s, inp, got)
+        if not opts:
+            e2e.check_block_e2e(orc, s, inp, got)
         for a, b in zip(got, want):
             assert np.array_equal(a, b, equal_nan=True), f"replay {rep}"
